@@ -1,0 +1,72 @@
+"""The oracle's pins must catch plausible mistakes: each case below plants one
+mistake in a copy of lid_oracle.c (on the CPU), builds it, and requires that
+at least one pin of tests/test_oracle.py fails against the broken copy."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle as T  # noqa: E402
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "lid_oracle.c")
+
+MUTATIONS = {
+    "no_relu": ("if (dot > 0.0)              /*", "if (1)              /*"),
+    "abs_for_relu": ("if (dot > 0.0)              /* ReLU: a non-positive dot contributes nothing */\n            I += wd[h] * dot;",
+                     "I += wd[h] * fabs(dot);"),
+    "w_inside_relu": ("if (dot > 0.0)              /* ReLU: a non-positive dot contributes nothing */\n            I += wd[h] * dot;",
+                      "if (wd[h] * dot > 0.0)\n            I += wd[h] * dot;"),
+    "transposed_q": ("qd[(int64_t)h * D + d] * kd[d]", "qd[(int64_t)d * H + h] * kd[d]"),
+    "dropped_last_head": ("for (int h = 0; h < H; ++h) {\n        double dot", "for (int h = 0; h < H - 1; ++h) {\n        double dot"),
+    "dropped_last_dim": ("for (int d = 0; d < D; ++d)\n            dot +=", "for (int d = 1; d < D; ++d)\n            dot +="),
+    "tie_by_larger_index": ("return (x->s < y->s) ? -1 : (x->s > y->s);", "return (x->s > y->s) ? -1 : (x->s < y->s);"),
+    "ascending_scores": ("if (x->v > y->v) return -1;\n    if (x->v < y->v) return 1;",
+                         "if (x->v < y->v) return -1;\n    if (x->v > y->v) return 1;"),
+    "mask_ignored": ("v = v + (float)lid_oracle_f16_to_f64(mask[t * mask_ld + s]);", "(void)0;"),
+    "mask_subtracted": ("v = v + (float)lid_oracle_f16_to_f64(mask[t * mask_ld + s]);",
+                        "v = v - (float)lid_oracle_f16_to_f64(mask[t * mask_ld + s]);"),
+    "range_lo_off_by_one": ("for (int64_t s = lo; s < hi; ++s) {\n            double I", "for (int64_t s = lo + 1; s < hi; ++s) {\n            double I"),
+    "range_ignored": ("    if (kv_range) {\n        a = kv_range[2 * t];", "    if (0) {\n        a = kv_range[2 * t];"),
+    "f16_exponent_bias": ("v = ldexp((double)(1024 + m), e - 25);", "v = ldexp((double)(1024 + m), e - 24);"),
+    "f16_subnormal": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -23);"),
+    "no_padding": ("idx_out[t * k_top + j] = valid ? (int32_t)c[j].s : -1;", "idx_out[t * k_top + j] = valid ? (int32_t)c[j].s : 0;"),
+    "neg_zero_kept": ("*out = v + 0.0f;", "*out = v;"),
+}
+
+PINS = [
+    T.test_golden_hand_example,
+    lambda o: T.test_closed_form_single_head_single_dim(o, 0),
+    T.test_zero_query_ties_resolve_by_index,
+    T.test_underflowing_negative_score_is_positive_zero,
+    *[(lambda s: (lambda o: T.test_bruteforce_exact_small_integers(o, s)))(s) for s in range(6)],
+    lambda o: T.test_bruteforce_random(o, "f16"),
+    T.test_f16_decode_exhaustive,
+    T.test_invariants_random,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {name}"
+    bad_src = tmp_path / f"bad_{name}.c"
+    bad_src.write_text(src.replace(old, new, 1))
+    lib = oracle.load_library(oracle.compile_source(str(bad_src), str(tmp_path / f"bad_{name}.so")))
+    bad = oracle.Oracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(bad)
+        except (AssertionError, RuntimeError, ValueError) as e:  # a pin failed: mistake caught
+            caught.append(type(e).__name__)
+            break
+    assert caught, f"no pin catches the planted mistake {name!r}"
+
+
+def test_unmutated_copy_passes_all_pins(tmp_path):
+    lib = oracle.load_library(oracle.compile_source(SRC, str(tmp_path / "good.so")))
+    good = oracle.Oracle(lib)
+    for pin in PINS:
+        pin(good)
