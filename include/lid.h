@@ -1,0 +1,130 @@
+/*
+ * lid.h -- C ABI of the fused lightning-indexer top-k for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (DeepSeek-V4-Flash lightning indexer):
+ *
+ *   I[t,s] = sum_h w[t,h] * max(0, sum_d q[t,h,d] * k[s,d])      (f32 accumulation)
+ *   v[t,s] = I[t,s] + mask[t,s]                                    (f32; f16 mask)
+ *   idx[t,:] = the k_top keys s with the largest v[t,s], ordered by v
+ *              descending and, on equal v, by s ascending
+ *
+ * Sources: ggml-org llama.cpp issue 25468, comment "Root cause: the
+ * lightning-indexer (lid_kq) score matrix" (the chain lid_kq -> relu ->
+ * * weights -> sum_rows -> lid_score -> + mask -> lid_top_k, with 64 heads,
+ * an f32 score and a top-512 int32 selection); the comment "Pinned: master is
+ * missing the fused ggml_lightning_indexer op" (the fused op's inputs q, k,
+ * weights); fairydreaming/llama.cpp PR 2 thread, last comment (the updated
+ * op has no scale-factor parameters and takes an f16 mask).  Here scoring
+ * and selection are one fused pass: no n_tok x n_kv score matrix, and no
+ * n_tok x H x n_kv per-head matrix, is ever written.
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument of lid_topk is a DEVICE pointer, owned by the
+ *    caller.  The library never allocates device memory; scratch space comes
+ *    in through `workspace`.
+ *  - All arrays are C row-major and contiguous (mask rows have stride
+ *    mask_ld).  q and k must be 16-byte aligned.
+ *  - A key s is visible to query t iff lo_t <= s < hi_t and v[t,s] != -inf.
+ *    Keys outside [lo_t, hi_t) are never scored and their mask entries are
+ *    never read.  Masked keys (-inf) are never returned.
+ *  - Rows with fewer than k_top visible keys are padded with idx = -1 and
+ *    score = -inf after the visible keys.
+ *  - A score of -0 is reported as +0 (and ties with +0 by index).
+ *  - Scale factors such as 1/sqrt(D) are not parameters: a positive scale
+ *    c commutes with the ReLU (c * w * max(0,x) = (c*w) * max(0,x)), so the
+ *    caller folds it into w.
+ *  - lid_topk is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  It does not synchronise the host.  Identical inputs give
+ *    bitwise-identical outputs.
+ *  - Errors: every argument check happens before any launch; on a negative
+ *    status nothing was launched and the outputs are untouched, except
+ *    LID_ERR_HIP (a launch failed; outputs undefined).  There is no fallback
+ *    to a path that would need an n_tok x n_kv buffer.
+ *  - Calls that share one workspace must not overlap in time.
+ */
+#ifndef LID_H
+#define LID_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of q and k.  w is always f32, mask always f16 (IEEE binary16 bits). */
+typedef enum { LID_F32 = 0, LID_F16 = 1, LID_BF16 = 2 } lid_dtype;
+
+typedef enum {
+    LID_OK = 0,
+    LID_ERR_INVALID_ARG = -1,  /* a NULL required pointer, bad size, misalignment ... */
+    LID_ERR_UNSUPPORTED = -2,  /* valid request outside the library's limits (k_top > 1024 ...) */
+    LID_ERR_WORKSPACE = -3,    /* workspace missing or smaller than lid_topk_workspace_size() */
+    LID_ERR_HIP = -4           /* a HIP launch failed */
+} lid_status;
+
+/* Kernel plan; LID_PLAN_AUTO picks one from the shape.  The others force a
+ * plan (for tests); a forced plan that cannot run the shape returns
+ * LID_ERR_UNSUPPORTED. */
+typedef enum {
+    LID_PLAN_AUTO = 0,
+    LID_PLAN_GENERIC = 1,   /* vector-ALU scoring, any H, D and dtype */
+    LID_PLAN_PREFILL = 2,   /* MFMA scoring, key tiles shared through LDS by a block of queries */
+    LID_PLAN_DECODE = 3     /* MFMA scoring, keys split across many workgroups per query */
+} lid_plan;
+
+typedef struct {
+    int64_t n_tok;     /* queries, >= 0 (0: nothing to do)                    */
+    int64_t n_kv;      /* keys, 0 <= n_kv <= 2^31 - 1                          */
+    int32_t n_head;    /* H >= 1                                               */
+    int32_t head_dim;  /* D >= 1                                               */
+    int32_t k_top;     /* 1 <= k_top <= 1024                                   */
+    int32_t qk_dtype;  /* lid_dtype of q and k                                 */
+    int64_t mask_ld;   /* row stride of mask in elements, >= n_kv; ignored if mask == NULL */
+    int32_t plan;      /* lid_plan; LID_PLAN_AUTO normally                     */
+    int32_t splits;    /* key splits per query; 0 = chosen by the library      */
+} lid_shape;
+
+/* Bytes of device workspace lid_topk needs for this shape (0 is possible:
+ * then workspace may be NULL).  Returns 0 for an invalid shape as well;
+ * lid_topk reports the error.  Depends only on the shape fields. */
+size_t lid_topk_workspace_size(const lid_shape* shape);
+
+/* The fused score + mask + top-k.
+ *   q         [n_tok, H, D]     qk_dtype
+ *   k         [n_kv, D]         qk_dtype
+ *   w         [n_tok, H]        f32, any sign
+ *   mask      [n_tok, mask_ld]  f16 additive mask, or NULL (no mask)
+ *   kv_range  [n_tok, 2]        int32 half-open [lo, hi) per query, or NULL
+ *                               (= [0, n_kv)); clamped to [0, n_kv); lo >= hi
+ *                               is an empty range
+ *   idx       [n_tok, k_top]    int32 output
+ *   score     [n_tok, k_top]    f32 output (the v of each returned key), or NULL
+ *   workspace device scratch of >= lid_topk_workspace_size(shape) bytes
+ *   stream    hipStream_t
+ * Inputs must be finite (q, k, w); a NaN or +inf score is not detected. */
+int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* w,
+             const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* The plan lid_topk would run for `shape` (a lid_plan value), and through
+ * `splits_out` (may be NULL) its key splits per query; negative lid_status if
+ * the shape is invalid or unsupported. */
+int lid_topk_plan(const lid_shape* shape, int32_t* splits_out);
+
+/* Static text for a status code. */
+const char* lid_status_string(int status);
+
+/* Text of the HIP error behind the last LID_ERR_HIP returned to this
+ * thread ("no error" if there was none).  Static storage; never NULL. */
+const char* lid_last_hip_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int lid_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LID_H */

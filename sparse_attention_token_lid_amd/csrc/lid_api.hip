@@ -1,0 +1,199 @@
+// lid_api.hip -- the C ABI (include/lid.h): argument checks, plan choice,
+// workspace sizing and kernel launches.  No device memory is allocated here;
+// nothing synchronises the host.
+#include <stdint.h>
+#include <string.h>
+
+#include "lid.h"
+#include "lid_device.h"
+#include "lid_kernels.h"
+
+namespace {
+
+using namespace lid;
+
+constexpr int kMaxTopK = 1024;
+constexpr int kMaxSplits = 1024;
+constexpr int kDecodeMaxTok = 4;       // auto plan: at most this many queries use the decode kernel
+constexpr int kDecodeKeysPerSplit = 1024;
+constexpr int kDecodeMaxSplits = 256;  // bounds the decode workspace independently of n_kv
+constexpr size_t kMaxLds = 160 * 1024;
+
+struct Plan {
+  int kind;         // lid_plan (never AUTO)
+  int P;            // key splits per query
+  int nw;           // prefill: wavefronts (queries) per workgroup
+  int cap;          // per-wave candidate capacity
+  int keys_per_wg;  // decode: LDS key slots per workgroup
+  int ch;           // merge: entries per list per round
+  size_t ws;        // workspace bytes
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = e;
+  return LID_ERR_HIP;
+}
+
+int merge_chunk(int P, int K) {
+  // read about 4K entries in the first round, at least 4 per list
+  int ch = next_pow2((int)cdiv(4LL * K, P));
+  if (ch < 4) ch = 4;
+  if (ch > next_pow2(K)) ch = next_pow2(K);
+  while (ch > 4 && (size_t)P * ch > 8192) ch >>= 1;
+  return ch;
+}
+
+int check_shape(const lid_shape* s) {
+  if (!s) return LID_ERR_INVALID_ARG;
+  if (s->n_tok < 0 || s->n_kv < 0 || s->n_kv > INT32_MAX || s->n_tok > INT32_MAX) return LID_ERR_INVALID_ARG;
+  if (s->n_head < 1 || s->head_dim < 1 || s->k_top < 1) return LID_ERR_INVALID_ARG;
+  if (s->qk_dtype != LID_F32 && s->qk_dtype != LID_F16 && s->qk_dtype != LID_BF16) return LID_ERR_INVALID_ARG;
+  if (s->plan < LID_PLAN_AUTO || s->plan > LID_PLAN_DECODE || s->splits < 0) return LID_ERR_INVALID_ARG;
+  if (s->k_top > kMaxTopK || s->splits > kMaxSplits) return LID_ERR_UNSUPPORTED;
+  return LID_OK;
+}
+
+int make_plan(const lid_shape* s, Plan* pl) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  const int K = s->k_top;
+  const bool mfma_ok = (s->qk_dtype == LID_F16 || s->qk_dtype == LID_BF16) && s->n_head == kMfmaHeads &&
+                       s->head_dim == kMfmaDim;
+  memset(pl, 0, sizeof(*pl));
+  pl->cap = 2 * K + 64;
+  int kind = s->plan;
+  if (kind == LID_PLAN_AUTO) {
+    if (!mfma_ok) kind = LID_PLAN_GENERIC;
+    else if (s->n_tok <= kDecodeMaxTok && cdiv(s->n_kv, kDecodeMaxSplits) <= kDecodeMaxKeys) kind = LID_PLAN_DECODE;
+    else kind = LID_PLAN_PREFILL;
+  }
+  if ((kind == LID_PLAN_PREFILL || kind == LID_PLAN_DECODE) && !mfma_ok) return LID_ERR_UNSUPPORTED;
+  pl->kind = kind;
+
+  if (kind == LID_PLAN_GENERIC) {
+    int64_t want = cdiv(s->n_kv, 8192);
+    pl->P = s->splits ? s->splits : (int)(want < 1 ? 1 : (want > 64 ? 64 : want));
+    if (generic_lds_bytes(pl->cap) > kMaxLds) return LID_ERR_UNSUPPORTED;
+  } else if (kind == LID_PLAN_PREFILL) {
+    pl->nw = (K <= 512) ? 8 : 4;
+    const int64_t tiles = cdiv(s->n_kv, kPrefillTile);
+    int P = s->splits;
+    if (!P) {
+      const int64_t nqb = cdiv(s->n_tok, pl->nw);
+      P = (nqb >= 1024 || tiles < 64) ? 1 : 8;
+    }
+    pl->P = P;
+    if (prefill_lds_bytes(pl->nw, pl->cap) > kMaxLds) return LID_ERR_UNSUPPORTED;
+  } else {  // decode
+    int P = s->splits;
+    if (!P) {
+      int64_t want = cdiv(s->n_kv, kDecodeKeysPerSplit);
+      P = (int)(want < 1 ? 1 : (want > kDecodeMaxSplits ? kDecodeMaxSplits : want));
+    }
+    pl->P = P;
+    int64_t kp = cdiv(cdiv(s->n_kv, 32), P) * 32;
+    if (kp < 32) kp = 32;
+    if (kp > kDecodeMaxKeys) return LID_ERR_UNSUPPORTED;
+    pl->keys_per_wg = (int)kp;
+    if (decode_lds_bytes(pl->keys_per_wg, K) > kMaxLds) return LID_ERR_UNSUPPORTED;
+  }
+  if (pl->P > 1) {
+    pl->ch = merge_chunk(pl->P, K);
+    if (merge_lds_bytes(pl->P, K, pl->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
+    pl->ws = (size_t)s->n_tok * pl->P * K * sizeof(uint64_t);
+  }
+  // grid sizes must fit a 32-bit grid
+  const int64_t blocks = (kind == LID_PLAN_PREFILL) ? cdiv(s->n_tok, pl->nw) * pl->P
+                         : (kind == LID_PLAN_DECODE) ? s->n_tok * pl->P
+                                                     : cdiv(s->n_tok * pl->P, 4);
+  if (blocks > INT32_MAX) return LID_ERR_UNSUPPORTED;
+  return LID_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lid_topk_workspace_size(const lid_shape* shape) {
+  Plan pl;
+  if (make_plan(shape, &pl) != LID_OK) return 0;
+  return pl.ws;
+}
+
+int lid_topk_plan(const lid_shape* shape, int32_t* splits_out) {
+  Plan pl;
+  int rc = make_plan(shape, &pl);
+  if (rc != LID_OK) return rc;
+  if (splits_out) *splits_out = pl.P;
+  return pl.kind;
+}
+
+int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
+             const int32_t* kv_range, int32_t* idx, float* score, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  Plan pl;
+  int rc = make_plan(shape, &pl);
+  if (rc != LID_OK) return rc;
+  const lid_shape& s = *shape;
+  if (s.n_tok == 0) return LID_OK;
+  if (!q || !w || !idx || (s.n_kv > 0 && !k)) return LID_ERR_INVALID_ARG;
+  if (mask && s.mask_ld < s.n_kv) return LID_ERR_INVALID_ARG;
+  if (pl.kind != LID_PLAN_GENERIC &&
+      ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k) & 15)))
+    return LID_ERR_INVALID_ARG;
+  if (pl.ws > 0 && (!workspace || workspace_bytes < pl.ws)) return LID_ERR_WORKSPACE;
+  if (pl.ws > 0 && (reinterpret_cast<uintptr_t>(workspace) & 7)) return LID_ERR_INVALID_ARG;
+
+  KArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.w = w;
+  a.mask = mask;
+  a.kv_range = kv_range;
+  a.idx = idx;
+  a.score = score;
+  a.lists = reinterpret_cast<uint64_t*>(workspace);
+  a.n_tok = s.n_tok;
+  a.n_kv = s.n_kv;
+  a.mask_ld = mask ? s.mask_ld : 0;
+  a.H = s.n_head;
+  a.D = s.head_dim;
+  a.K = s.k_top;
+  a.P = pl.P;
+  a.cap = pl.cap;
+  a.dtype = s.qk_dtype;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t e;
+  if (pl.kind == LID_PLAN_PREFILL) e = launch_prefill(a, pl.nw, st);
+  else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, st);
+  else e = launch_generic(a, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (pl.P > 1) {
+    e = launch_merge(a, pl.ch, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return LID_OK;
+}
+
+const char* lid_status_string(int status) {
+  switch (status) {
+    case LID_OK: return "ok";
+    case LID_ERR_INVALID_ARG: return "invalid argument";
+    case LID_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case LID_ERR_WORKSPACE: return "workspace missing or too small";
+    case LID_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* lid_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
+
+int lid_version(void) { return 100; }
+
+}  // extern "C"

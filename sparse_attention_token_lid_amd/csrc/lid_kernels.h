@@ -1,0 +1,44 @@
+// lid_kernels.h -- internal interface between the C-ABI host code and the
+// HIP kernels of the fused lightning-indexer top-k.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lid {
+
+// Arguments shared by every kernel (passed by value).
+struct KArgs {
+  const void* q;            // [n_tok, H, D] f32 / f16 bits / bf16 bits
+  const void* k;            // [n_kv, D]
+  const float* w;           // [n_tok, H]
+  const uint16_t* mask;     // [n_tok, mask_ld] f16 bits, or null
+  const int32_t* kv_range;  // [n_tok, 2], or null
+  int32_t* idx;             // [n_tok, K]
+  float* score;             // [n_tok, K], or null
+  uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1)
+  int64_t n_tok, n_kv, mask_ld;
+  int32_t H, D, K, P;
+  int32_t cap;              // per-wave candidate buffer capacity (entries)
+  int32_t dtype;            // 0 f32, 1 f16, 2 bf16
+};
+
+// Shapes the MFMA kernels are written for.
+constexpr int kMfmaHeads = 64;
+constexpr int kMfmaDim = 128;
+constexpr int kPrefillTile = 64;       // keys per LDS tile
+constexpr int kDecodeMaxKeys = 16384;  // keys one decode workgroup scores (LDS bound)
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);
+size_t prefill_lds_bytes(int nw, int cap);
+
+hipError_t launch_decode(const KArgs& a, int keys_per_wg, hipStream_t st);
+size_t decode_lds_bytes(int keys_per_wg, int K);
+
+hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st);
+size_t merge_lds_bytes(int P, int K, int ch);
+
+hipError_t launch_generic(const KArgs& a, hipStream_t st);
+size_t generic_lds_bytes(int cap);
+
+}  // namespace lid

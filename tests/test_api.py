@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/lid.h declares, sizes workspaces, picks plans, and
+rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lid_inputs as li
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_attention_token_lid_amd as L
+    if not os.path.exists(L.LIB_PATH):
+        from sparse_attention_token_lid_amd import build
+        build.build()
+    L.load()
+    return L
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "lid.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lid_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_shape_struct_layout(L):
+    assert ctypes.sizeof(L.LidShape) == 48
+    assert L.LidShape.mask_ld.offset == 32 and L.LidShape.splits.offset == 44
+
+
+def shape_of(name, **kw):
+    import sparse_attention_token_lid_amd as L
+    wl = li.WORKLOADS[name]
+    dt = {"f32": L.LID_F32, "f16": L.LID_F16, "bf16": L.LID_BF16}[wl.dtype]
+    args = dict(n_tok=wl.n_tok, n_kv=wl.n_kv, n_head=wl.n_head, head_dim=wl.head_dim, k_top=wl.k_top,
+                qk_dtype=dt)
+    args.update(kw)
+    return L.make_shape(**args)
+
+
+@pytest.mark.parametrize("name,plan", [("c1", "generic"), ("c2", "decode"), ("c3", "prefill"),
+                                       ("c4", "prefill"), ("c5", "prefill"), ("dec1m", "decode")])
+def test_auto_plans_and_workspace(L, name, plan):
+    s = shape_of(name)
+    got, splits = L.plan_of(s)
+    assert got == plan
+    ws = L.workspace_size(s)
+    wl = li.WORKLOADS[name]
+    assert ws == (wl.n_tok * splits * wl.k_top * 8 if splits > 1 else 0)
+    # O(n_tok * k_top * splits) with splits <= 256, whatever n_kv is
+    assert splits <= 256 and ws <= wl.n_tok * wl.k_top * 8 * 256
+    if wl.n_kv >= 131072:
+        assert ws <= wl.n_tok * wl.n_kv * 4 // 4   # well below even the f32 score matrix
+
+
+def call(L, shape, q=16, k=16, w=16, mask=None, rng=None, idx=16, score=None, ws=None, ws_bytes=0):
+    # fake, never-dereferenced addresses: every case here fails before a launch
+    return L.load().lid_topk(ctypes.byref(shape), q, k, w, mask, rng, idx, score, ws, ws_bytes, None)
+
+
+def test_errors_before_launch(L):
+    ok = shape_of("c3")
+    assert call(L, shape_of("c3", qk_dtype=7)) == -1
+    assert call(L, shape_of("c3", k_top=0)) == -1
+    assert call(L, shape_of("c3", k_top=2048)) == -2
+    assert call(L, shape_of("c3", n_head=0)) == -1
+    assert call(L, shape_of("c3", n_kv=-1)) == -1
+    assert call(L, shape_of("c3", n_kv=2**31)) == -1
+    assert call(L, shape_of("c3", plan=9)) == -1
+    assert call(L, shape_of("c3", splits=5000)) == -2
+    assert call(L, ok, q=None) == -1
+    assert call(L, ok, w=None) == -1
+    assert call(L, ok, idx=None) == -1
+    assert call(L, ok, q=8) == -1                       # misaligned q
+    assert call(L, ok, mask=64) == -1                   # mask given, mask_ld 0 < n_kv
+    assert call(L, ok) == -3                            # workspace needed, none given
+    ws = L.workspace_size(ok)
+    assert ws > 0
+    assert call(L, ok, ws=64, ws_bytes=ws - 1) == -3
+    assert call(L, shape_of("c3", plan=3, n_head=32)) == -2   # MFMA plan needs H=64, D=128
+    assert call(L, shape_of("c3", plan=2, qk_dtype=0)) == -2  # ... and f16 / bf16
+    assert call(L, shape_of("c3", n_tok=0)) == 0              # nothing to do: no launch
+    assert L.load().lid_topk(None, None, None, None, None, None, None, None, None, 0, None) == -1
+
+
+def test_status_strings_and_version(L):
+    lib = L.load()
+    for code in (0, -1, -2, -3, -4, 5):
+        assert isinstance(lib.lid_status_string(code), bytes)
+    assert lib.lid_version() >= 100
+
+
+def test_workspace_size_invalid_is_zero(L):
+    assert L.workspace_size(shape_of("c3", k_top=0)) == 0

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+seeded inputs.  Every test here needs an MI355X and the built liblid.so."""
+import sys
+
+import numpy as np
+import pytest
+
+import lid_inputs as li
+from parity import REL_TOL, check_rows, oracle_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lid():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_lid_amd as L
+    L.load()
+    return L
+
+
+def to_dev(a, dtype):
+    """numpy array -> contiguous cuda tensor (bf16 / f16 masks given as uint16 bits)."""
+    if a is None:
+        return None
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    if dtype == "mask":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.float16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_gpu(lid, q, k, w, mask, ranges, k_top, dtype, plan=0, splits=0):
+    qd, kd = to_dev(q, dtype), to_dev(k, dtype)
+    idx, sc = lid.topk(qd, kd, to_dev(w, "f32"), mask=to_dev(mask, "mask"),
+                       kv_range=to_dev(ranges, "i32"), k_top=k_top, plan=plan, splits=splits)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def parity(lid, q, k, w, mask, ranges, k_top, dtype, plan=0, splits=0, rows=None, exact=False, label=""):
+    _say(f"[parity] {label} plan={plan} splits={splits} n_tok={q.shape[0]} n_kv={k.shape[0]} k_top={k_top}")
+    g_idx, g_sc = run_gpu(lid, q, k, w, mask, ranges, k_top, dtype, plan, splits)
+    if rows is None:
+        rows = list(range(q.shape[0]))
+    o_idx, o_sc, maxabs, v = oracle_rows(q, k, w, mask, ranges, k_top, rows,
+                                         qk_dtype=dtype if dtype == "bf16" else None)
+    tol = REL_TOL[dtype] * maxabs
+    n_exact = check_rows(g_idx[rows], g_sc[rows], o_idx, o_sc, v, tol, rows=rows, exact=exact)
+    _say(f"[parity]   ok: {n_exact}/{len(rows)} rows with identical index sets, tol={tol:.3g}")
+    return g_idx, g_sc
+
+
+# ---------------------------------------------------------------- small cases
+
+@pytest.mark.parametrize("form", ["mask", "ranges"])
+def test_tiny_f32_generic(lid, form):
+    d = li.make("c1")
+    parity(lid, d["q"], d["k"], d["w"], d["mask"] if form == "mask" else None,
+           d["ranges"] if form == "ranges" else None, 16, "f32", label=f"c1/{form}")
+
+
+def exact_inputs(n_tok, n_kv, seed, dtype="f16"):
+    """Small-integer q, k and dyadic w: every score is exact in f32."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-1, 2, (n_tok, 64, 128)).astype(np.float32)
+    k = rng.integers(-1, 2, (n_kv, 128)).astype(np.float32)
+    w = rng.choice(np.array([0, 0.25, 0.5, 1, 2, -0.5], np.float32), (n_tok, 64))
+    if dtype == "f16":
+        return q.astype(np.float16), k.astype(np.float16), w
+    return li._round_qk(q, "bf16"), li._round_qk(k, "bf16"), w
+
+
+@pytest.mark.parametrize("plan,splits", [(2, 1), (2, 3), (2, 8), (3, 1), (3, 5), (1, 1), (1, 2)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_arithmetic_bit_exact(lid, plan, splits, dtype):
+    """Exactly representable scores: index order and scores (ties included)
+    must equal the oracle bit for bit, on every kernel plan."""
+    n_tok, n_kv = 11, 3000
+    q, k, w = exact_inputs(n_tok, n_kv, seed=plan * 10 + splits, dtype=dtype)
+    ranges = np.array([[0, n_kv], [5, 2999], [64, 128], [1000, 1001], [0, 0], [2990, 3000],
+                       [0, 700], [100, 2500], [3, 1900], [0, 3000], [7, 12]], np.int32)
+    parity(lid, q, k, w, None, ranges, 512, dtype, plan, splits, exact=True, label=f"exact/{dtype}")
+
+
+@pytest.mark.parametrize("plan,splits", [(2, 0), (2, 1), (2, 4), (3, 0), (3, 3), (1, 0)])
+def test_random_causal_mask_ragged(lid, plan, splits):
+    """Random f16 inputs, causal dense mask, ragged n_kv (not a tile multiple)."""
+    n_tok, n_kv = 37 if plan != 3 else 3, 5000
+    wl = li.Workload("t", n_tok, n_kv, 64, 128, 512, "f16", True, "causal")
+    q, k, w = li.draw_qkw(n_tok, n_kv, 64, 128, "f16", True, seed=21)
+    ranges = li.visible_ranges(wl)
+    mask = li.mask_from_ranges(ranges, n_kv, mask_ld=n_kv + 40)
+    parity(lid, q, k, w, mask, None, 512, "f16", plan, splits, label="random/causal")
+
+
+def test_mask_and_ranges_forms_identical(lid):
+    n_tok, n_kv = 24, 4100
+    wl = li.Workload("t", n_tok, n_kv, 64, 128, 512, "f16", True, "causal")
+    q, k, w = li.draw_qkw(n_tok, n_kv, 64, 128, "f16", True, seed=5)
+    ranges = li.visible_ranges(wl)
+    mask = li.mask_from_ranges(ranges, n_kv)
+    a = run_gpu(lid, q, k, w, mask, None, 512, "f16")
+    b = run_gpu(lid, q, k, w, None, ranges, 512, "f16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_deterministic(lid):
+    q, k, w = li.draw_qkw(16, 9000, 64, 128, "f16", True, seed=9)
+    for plan, splits in [(2, 8), (3, 9)]:
+        a = run_gpu(lid, q, k, w, None, None, 512, "f16", plan, splits)
+        b = run_gpu(lid, q, k, w, None, None, 512, "f16", plan, splits)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("plan", [1, 2, 3])
+def test_edge_cases(lid, plan):
+    # keys fewer than k_top, fully masked row, empty range, ties (q = 0), k_top = 1
+    n_tok, n_kv = 9, 300
+    q, k, w = li.draw_qkw(n_tok, n_kv, 64, 128, "f16", True, seed=3)
+    q[2] = 0  # all scores +0: first keys by index
+    mask = np.zeros((n_tok, n_kv), np.uint16)
+    mask[4, :] = 0xFC00           # fully masked row
+    mask[5, ::2] = 0xFC00         # every other key masked
+    mask[6, :] = 0x3C00           # +1.0 everywhere: shifts scores, masks nothing
+    mask[7, 10:] = 0xBC00         # -1.0 beyond key 10
+    ranges = np.array([[0, 300], [0, 300], [0, 300], [50, 50], [0, 300], [0, 300], [0, 300],
+                       [0, 300], [299, 400]], np.int32)
+    for k_top in (1, 7, 512):
+        parity(lid, q, k, w, mask, ranges, k_top, "f16", plan, 0, label=f"edge/k{k_top}")
+
+
+@pytest.mark.parametrize("plan", [1, 2, 3])
+def test_no_keys(lid, plan):
+    q, k, w = li.draw_qkw(3, 1, 64, 128, "f16", True, seed=1)
+    k0 = k[:0]
+    qd, kd = to_dev(q, "f16"), torch.empty((0, 128), dtype=torch.float16, device="cuda")
+    idx, sc = lid.topk(qd, kd, to_dev(w, "f32"), k_top=8, plan=plan)
+    torch.cuda.synchronize()
+    assert (idx.cpu() == -1).all() and torch.isinf(sc.cpu()).all()
+    del k0
+
+
+def test_k_top_1024(lid):
+    q, k, w = li.draw_qkw(10, 7000, 64, 128, "f16", True, seed=77)
+    for plan in (2, 3):
+        parity(lid, q, k, w, None, None, 1024, "f16", plan, 0, label="k1024")
+
+
+def test_adversarial_ascending_scores(lid):
+    """Scores that grow with the key index make every key a new top-k member
+    (the streaming buffer is cut back again and again)."""
+    n_tok, n_kv = 9, 20000
+    q = np.zeros((n_tok, 64, 128), np.float16)
+    q[:, :, 0] = 1.0
+    k = np.zeros((n_kv, 128), np.float16)
+    k[:, 0] = (np.arange(n_kv) / n_kv * 8).astype(np.float16)   # non-decreasing, many ties
+    w = np.full((n_tok, 64), 1.0 / 64, np.float32)
+    for plan, splits in [(2, 1), (2, 8), (3, 0), (1, 0)]:
+        parity(lid, q, k, w, None, None, 512, "f16", plan, splits, exact=True, label="ascending")
+
+
+# ---------------------------------------------------------------- workloads at full size
+
+def sample_rows(n, extra=4, seed=0):
+    rng = np.random.default_rng(seed)
+    base = {0, 1, n // 2, n - 1}
+    base |= set(rng.integers(0, n, extra).tolist())
+    return sorted(base)
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "dec1m"])
+def test_workload_sampled(lid, name):
+    d = li.make(name)
+    wl = d["wl"]
+    rows = sample_rows(wl.n_tok)
+    parity(lid, d["q"], d["k"], d["w"], d["mask"], None, wl.k_top, wl.dtype, rows=rows, label=name)
+
+
+def test_workload_multiseq_ranges(lid):
+    d = li.make("c5")
+    wl = d["wl"]
+    rows = sample_rows(wl.n_tok) + [511, 512, 1023, 1024, 1535, 1536]
+    rows = sorted(set(rows))
+    parity(lid, d["q"], d["k"], d["w"], None, d["ranges"], wl.k_top, wl.dtype, rows=rows, label="c5/ranges")
+
+
+def test_workload_multiseq_dense_mask(lid):
+    """c5 with the dense f16 mask (4 GiB, built on the device) gives the same
+    result as the ranges form."""
+    d = li.make("c5")
+    wl = d["wl"]
+    qd, kd, wd = to_dev(d["q"], "f16"), to_dev(d["k"], "f16"), to_dev(d["w"], "f32")
+    rd = to_dev(d["ranges"], "i32")
+    a_idx, a_sc = lid.topk(qd, kd, wd, kv_range=rd, k_top=wl.k_top)
+    mask = li.mask_from_ranges_torch(d["ranges"], wl.n_kv, "cuda")
+    b_idx, b_sc = lid.topk(qd, kd, wd, mask=mask, k_top=wl.k_top)
+    torch.cuda.synchronize()
+    assert torch.equal(a_idx, b_idx) and torch.equal(a_sc, b_sc)
+
+
+# ---------------------------------------------------------------- memory bound
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_no_score_matrix_allocated(lid, name):
+    """The call allocates nothing beyond the caller's outputs and workspace:
+    device free memory and torch's peak are unchanged across it, and the
+    workspace is O(n_tok * splits * k_top), far below n_tok * n_kv."""
+    d = li.make(name, with_mask=False)
+    wl = d["wl"]
+    qd, kd, wd = to_dev(d["q"], "f16"), to_dev(d["k"], "f16"), to_dev(d["w"], "f32")
+    rd = to_dev(d["ranges"], "i32")
+    shape = lid.shape_for(qd, kd, wl.k_top)
+    ws_bytes = lid.workspace_size(shape)
+    _, splits = lid.plan_of(shape)
+    assert ws_bytes == wl.n_tok * splits * wl.k_top * 8 if splits > 1 else ws_bytes == 0
+    assert ws_bytes < wl.n_tok * wl.n_kv * 4 / 8   # < 1/8 of even the f32 score matrix
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((wl.n_tok, wl.k_top), dtype=torch.int32, device="cuda")
+    sc = torch.empty((wl.n_tok, wl.k_top), dtype=torch.float32, device="cuda")
+    lid.topk(qd, kd, wd, kv_range=rd, k_top=wl.k_top, idx=idx, score=sc, workspace=ws)  # warm up
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    lid.topk(qd, kd, wd, kv_range=rd, k_top=wl.k_top, idx=idx, score=sc, workspace=ws)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.max_memory_allocated() == base
+    assert free1 == free0
+    _say(f"[memory] {name}: workspace {ws_bytes / 2**20:.1f} MiB vs f32 score matrix "
+         f"{wl.n_tok * wl.n_kv * 4 / 2**20:.0f} MiB; free memory unchanged")
