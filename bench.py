@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused lightning-indexer top-k (lid_topk) on one MI355X.
+
+One step = one lid_topk call over one batch of the workload (all of it:
+scoring, mask, streaming top-k and, for split plans, the merge).  Inputs are
+seeded synthetic tensors already resident in device memory; several device
+copies are rotated so that consecutive steps do not re-read the same bytes out
+of the 256 MB last-level cache.  Prints one JSON line on stdout (progress goes
+to stderr).
+
+    python bench.py [--workload c2|c3|c4|c5|dec1m] [--steps K] [--warmup W]
+
+The default workload is c2 (single-token decode over 32768 keys).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer scored (query,key) pairs/sec + top-k tokens/sec; % MFMA / % HBM peak"
+PEAK_HBM_BPS = 8.0e12        # MI355X HBM3E, published
+PEAK_MFMA_F16 = 2.5e15       # MI355X dense f16/bf16 MFMA, published
+DEFAULT_STEPS = {"c2": 2000, "dec1m": 300, "c3": 400, "c4": 40, "c5": 20}
+DEFAULT_FORM = {"c2": "none", "dec1m": "none", "c3": "mask", "c4": "mask", "c5": "ranges"}
+DESCRIPTION = {
+    "c2": "single-token decode, n_tok 1 x n_kv 32768",
+    "dec1m": "single-token decode, n_tok 1 x n_kv 1048576",
+    "c3": "prefill ubatch, n_tok 512 x n_kv 16384, causal f16 mask",
+    "c4": "long-context prefill, n_tok 2048 x n_kv 131072, causal f16 mask",
+    "c5": "multi-sequence ubatch, 4 seqs x 512 queries, 4 key blocks x 262144, per-query ranges",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(wl, ranges):
+    if ranges is None:
+        return wl.n_tok * wl.n_kv
+    return int((ranges[:, 1].astype("int64") - ranges[:, 0]).clip(min=0).sum())
+
+
+def cpu_baseline(d, form, seconds, rows_hint=None):
+    """Time the CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    wl = d["wl"]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    ranges = d["ranges"]
+    mask = d["mask"] if form == "mask" else None
+    rng_arg = ranges if form == "ranges" else None
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.topk(d["q"], d["k"], d["w"], mask=mask, kv_range=rng_arg, k_top=wl.k_top, rows=rows,
+                    threads=threads)
+        return time.perf_counter() - t0
+
+    def pairs_of(rows):
+        if ranges is None:
+            return len(rows) * wl.n_kv
+        r = ranges[rows]
+        return int((r[:, 1].astype(np.int64) - r[:, 0]).sum())
+
+    if wl.n_tok == 1:
+        # one query: the whole workload, repeated until the time budget is used
+        reps, spent = 0, 0.0
+        while spent < seconds and (reps == 0 or spent / reps * (reps + 1) <= 3 * seconds):
+            spent += run([0])
+            reps += 1
+        return {"value": pairs_of([0]) * reps / spent, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+                "sample": f"the full workload (1 query x {wl.n_kv} keys) run {reps} times, {spent:.1f} s"}
+    # many queries: spread a row sample over the host's cores, sized to the budget
+    m = min(wl.n_tok, threads)
+    rows = list(range(0, wl.n_tok, max(1, wl.n_tok // m)))[:m]
+    t = run(rows)
+    if t < seconds / 3:
+        m2 = min(wl.n_tok, int(len(rows) * seconds / max(t, 1e-3)))
+        rows = list(range(0, wl.n_tok, max(1, wl.n_tok // max(m2, 1))))[:max(m2, 1)]
+        t = run(rows)
+    return {"value": pairs_of(rows) / t, "unit": "pairs/s", "cores": min(threads, len(rows)), "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.n_tok} queries (evenly spaced) with all their visible keys, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="c2", choices=sorted(DEFAULT_STEPS))
+    ap.add_argument("--form", default=None, choices=["none", "mask", "ranges"])
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the indexer path here is a single-GPU build "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lid_inputs as li
+    import sparse_attention_token_lid_amd as L
+
+    name = args.workload
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS[name]
+    warmup = args.warmup if args.warmup is not None else max(3, steps // 10)
+    form = args.form or DEFAULT_FORM[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L.load()
+
+    log(f"[bench] generating {name} ({form})")
+    d = li.make(name, with_mask=(form == "mask"))
+    wl = d["wl"]
+    if form == "mask" and d["mask"] is None:
+        raise SystemExit("dense mask form is not generated on the host for this workload; use --form ranges")
+    pairs = visible_pairs(wl, d["ranges"] if form != "none" else None)
+
+    def dev_tensor(a, kind):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if kind in ("f16bits",) else a)
+        t = t.to(dev)
+        return t.view(torch.float16) if kind == "f16bits" else t
+
+    q0 = torch.from_numpy(d["q"]).to(dev)
+    k0 = torch.from_numpy(d["k"]).to(dev)
+    w0 = torch.from_numpy(d["w"]).to(dev)
+    m0 = dev_tensor(d["mask"], "f16bits") if form == "mask" else None
+    r0 = torch.from_numpy(d["ranges"]).to(dev) if form == "ranges" else None
+    per_copy = sum(t.numel() * t.element_size() for t in (q0, k0, w0, m0, r0) if t is not None)
+    copies = max(1, min(64, math.ceil((1 << 30) / per_copy)))
+    sets = [(q0, k0, w0, m0, r0)]
+    for _ in range(copies - 1):
+        sets.append(tuple(None if t is None else t.clone() for t in (q0, k0, w0, m0, r0)))
+    shape = L.shape_for(q0, k0, wl.k_top, m0, splits=args.splits)
+    plan, splits = L.plan_of(shape)
+    ws_bytes = L.workspace_size(shape)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty((wl.n_tok, wl.k_top), dtype=torch.int32, device=dev)
+    sc = torch.empty((wl.n_tok, wl.k_top), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lib = L.load()
+    calls = []
+    for (q, k, w, m, r) in sets:
+        ptrs = [t.data_ptr() if t is not None else None for t in (q, k, w, m, r)]
+        calls.append((ctypes.byref(shape), *ptrs, idx.data_ptr(), sc.data_ptr(), ws.data_ptr(), ws_bytes, stream))
+    log(f"[bench] plan={plan} splits={splits} workspace={ws_bytes} B copies={copies} "
+        f"({per_copy / 2**20:.1f} MiB each) steps={steps} warmup={warmup}")
+
+    def step(i):
+        rc = lib.lid_topk(*calls[i % copies])
+        if rc != 0:
+            raise L.LidError(rc)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    hip = L.hip_runtime()
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2 * steps):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        L.set_profile_events(evs[2 * i], evs[2 * i + 1])
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    L.set_profile_events(None, None)
+    total_ms = t0.elapsed_time(t1)
+    kern = []
+    for i in range(steps):
+        f = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(f), evs[2 * i], evs[2 * i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        kern.append(f.value)
+    for e in evs:
+        hip.hipEventDestroy(e)
+    kern_ms = sum(kern) / len(kern)
+    ms_per_step = total_ms / steps
+    log(f"[bench] {steps} steps: {total_ms:.3f} ms GPU ({(wall1 - wall0) * 1e3:.1f} ms wall), "
+        f"{ms_per_step * 1e3:.2f} us/step, scoring kernel {kern_ms * 1e3:.2f} us")
+
+    H, D, K = wl.n_head, wl.head_dim, wl.k_top
+    value = pairs * steps / (total_ms * 1e-3)
+    if plan == "decode":
+        key_bytes = pairs * D * 2
+        alg_bytes = key_bytes + wl.n_tok * (H * D * 2 + H * 4) + (pairs * 2 if form == "mask" else 0) \
+            + wl.n_tok * K * 8
+        achieved = alg_bytes / (kern_ms * 1e-3)
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_BPS, "traffic": None}
+    else:
+        flops = 2.0 * H * D * pairs
+        achieved = flops / (kern_ms * 1e-3)
+        roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_MFMA_F16 / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_F16, "traffic": None}
+    out = {
+        "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{name}: {DESCRIPTION[name]}", "n_tok": wl.n_tok, "n_kv": wl.n_kv, "n_head": H,
+                   "head_dim": D, "k_top": K, "visible_pairs": pairs, "visibility": form, "plan": plan,
+                   "splits": splits, "workspace_bytes": ws_bytes, "parallelism": "single GPU"},
+        "topk_tokens_per_s": wl.n_tok * steps / (total_ms * 1e-3),
+        "scoring_kernel_us": kern_ms * 1e3,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(d, form, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

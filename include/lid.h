@@ -116,6 +116,13 @@ int lid_topk_plan(const lid_shape* shape, int32_t* splits_out);
 /* Static text for a status code. */
 const char* lid_status_string(int status);
 
+/* Measurement hook.  With non-NULL hipEvent_t handles, every later lid_topk
+ * records `before_scoring` on its stream right before it launches its scoring
+ * kernel and `after_scoring` right after, so hipEventElapsedTime gives that
+ * kernel's duration; the split merge (if any) falls outside.  NULL, NULL turns
+ * it off.  Process-wide setting, not synchronised: set it from one thread. */
+void lid_set_profile_events(void* before_scoring, void* after_scoring);
+
 /* Text of the HIP error behind the last LID_ERR_HIP returned to this
  * thread ("no error" if there was none).  Static storage; never NULL. */
 const char* lid_last_hip_error(void);

@@ -28,7 +28,7 @@ PLAN_NAMES = {PLAN_GENERIC: "generic", PLAN_PREFILL: "prefill", PLAN_DECODE: "de
 STATUS = {0: "LID_OK", -1: "LID_ERR_INVALID_ARG", -2: "LID_ERR_UNSUPPORTED", -3: "LID_ERR_WORKSPACE",
           -4: "LID_ERR_HIP"}
 EXPORTS = ("lid_topk", "lid_topk_workspace_size", "lid_topk_plan", "lid_status_string", "lid_last_hip_error",
-           "lid_version")
+           "lid_set_profile_events", "lid_version")
 
 
 class LidShape(ctypes.Structure):
@@ -54,6 +54,10 @@ def load():
     """The ctypes handle of liblid.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch ships its own HIP runtime; importing it first makes liblid.so
+        # bind to that same runtime (one runtime per process, so torch's
+        # streams and memory are valid handles for the library)
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} not found: run `python -m sparse_attention_token_lid_amd.build` "
                                "(or __graft_entry__.build()); there is no fallback path")
@@ -69,6 +73,8 @@ def load():
         lib.lid_status_string.argtypes = [ctypes.c_int]
         lib.lid_last_hip_error.restype = ctypes.c_char_p
         lib.lid_last_hip_error.argtypes = []
+        lib.lid_set_profile_events.restype = None
+        lib.lid_set_profile_events.argtypes = [vp, vp]
         lib.lid_version.restype = ctypes.c_int
         lib.lid_version.argtypes = []
         _lib = lib
@@ -144,3 +150,15 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
     if rc != 0:
         raise LidError(rc)
     return idx, score
+
+
+def set_profile_events(before, after):
+    """Have lid_topk record two hipEvent_t handles (ints) around its scoring
+    kernel; (None, None) turns this off."""
+    load().lid_set_profile_events(before, after)
+
+
+def hip_runtime():
+    """ctypes handle of the process's HIP runtime (the one torch loaded)."""
+    load()
+    return ctypes.CDLL("libamdhip64.so.7")

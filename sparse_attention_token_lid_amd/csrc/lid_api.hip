@@ -32,6 +32,8 @@ struct Plan {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
+hipEvent_t g_prof_before = nullptr;  // recorded around the scoring kernel when set
+hipEvent_t g_prof_after = nullptr;
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = e;
@@ -170,10 +172,12 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   hipError_t e;
+  if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
   if (pl.kind == LID_PLAN_PREFILL) e = launch_prefill(a, pl.nw, st);
   else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, st);
   else e = launch_generic(a, st);
   if (e != hipSuccess) return hip_fail(e);
+  if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
   if (pl.P > 1) {
     e = launch_merge(a, pl.ch, st);
     if (e != hipSuccess) return hip_fail(e);
@@ -190,6 +194,11 @@ const char* lid_status_string(int status) {
     case LID_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }
+}
+
+void lid_set_profile_events(void* before_scoring, void* after_scoring) {
+  g_prof_before = reinterpret_cast<hipEvent_t>(before_scoring);
+  g_prof_after = reinterpret_cast<hipEvent_t>(after_scoring);
 }
 
 const char* lid_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
