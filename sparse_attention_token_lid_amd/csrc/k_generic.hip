@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NWG * 64) void generic_kernel(KArgs a) {
         float dot = 0.f;
         const int64_t qo = (t * H + h) * (int64_t)D;
         for (int d = 0; d < D; ++d) dot = __builtin_fmaf(load_qk(a.q, qo + d, a.dtype), load_qk(a.k, s * D + d, a.dtype), dot);
-        I = __builtin_fmaf(a.w[t * H + h], __builtin_fmaxf(dot, 0.f), I);
+        I = __builtin_fmaf(a.w[t * H + h], relu(dot), I);
       }
       float mv = a.mask ? f16_bits_to_f32(a.mask[t * a.mask_ld + s]) : 0.f;
       v = (I + mv) + 0.0f;

@@ -15,7 +15,7 @@
 namespace lid {
 namespace {
 
-constexpr int BS = 256;
+constexpr int BS = 512;
 
 __global__ __launch_bounds__(BS) void merge_kernel(KArgs a, int ch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -24,7 +24,8 @@ __global__ __launch_bounds__(BS) void merge_kernel(KArgs a, int ch) {
   const int capm = K + P * ch;
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem);          // [capm]
   uint64_t* sel = cand + capm;                                 // [n2]
-  uint64_t* last = sel + n2;                                   // [P] last key read per list
+  uint64_t* tmp = sel + n2;                                    // [2 * BS]
+  uint64_t* last = tmp + 2 * BS;                               // [P] last key read per list
   BlockShared* sh = reinterpret_cast<BlockShared*>(last + P);
   int* counters = reinterpret_cast<int*>(sh + 1);             // [2]
   int& s_count = counters[0];
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(BS) void merge_kernel(KArgs a, int ch) {
       if (msk) {
         const int leader = __ffsll((unsigned long long)msk) - 1;
         if (lane_id() == leader) base = atomicAdd(&s_count, __popcll(msk));
-        base = __shfl(base, leader);
+        base = __builtin_amdgcn_readlane(base, leader);
       }
       if (ins) cand[base + mbcnt(msk)] = key;
       // the last entry of this list's chunk decides whether the list goes on
@@ -77,7 +78,9 @@ __global__ __launch_bounds__(BS) void merge_kernel(KArgs a, int ch) {
     // keep the K best; their K-th key bounds the final threshold from below,
     // and every list whose last key read is below it is finished
     if (count > K && (r == 0 || count + P * ch > capm)) {
-      const uint64_t kap = block_kth_largest(cand, count, K, *sh);
+      uint64_t ka, ko;
+      block_key_stats(cand, count, &ka, &ko, *sh);
+      const uint64_t kap = block_kth_largest(cand, count, K, ka, ko, *sh);
       const int kept = block_compact(cand, count, kap, sel, *sh);
       for (int i = threadIdx.x; i < kept; i += BS) cand[i] = sel[i];
       if (threadIdx.x == 0) s_count = kept;
@@ -89,7 +92,15 @@ __global__ __launch_bounds__(BS) void merge_kernel(KArgs a, int ch) {
   }
   const int count = s_count;
   __syncthreads();
-  block_select_sorted(cand, count, K, sel, *sh);
+  if (count == K && tau != 0ull) {
+    // the last cut left exactly the K best and no list had more to give
+    for (int i = threadIdx.x; i < K; i += BS) sel[i] = cand[i];
+    for (int i = K + threadIdx.x; i < n2; i += BS) sel[i] = 0ull;
+    __syncthreads();
+    block_sort_desc(sel, n2, tmp);
+  } else {
+    block_select_sorted(cand, count, K, sel, tmp, *sh);
+  }
   for (int i = threadIdx.x; i < K; i += BS) {
     a.idx[t * K + i] = key_index(sel[i]);
     if (a.score) a.score[t * K + i] = key_score(sel[i]);
@@ -100,8 +111,8 @@ __global__ __launch_bounds__(BS) void merge_kernel(KArgs a, int ch) {
 
 size_t merge_lds_bytes(int P, int K, int ch) {
   size_t capm = (size_t)K + (size_t)P * ch;
-  return capm * 8 + (size_t)next_pow2(K) * 8 + (size_t)P * 8 + sizeof(BlockShared) + 2 * sizeof(int) +
-         2 * (size_t)P;
+  return capm * 8 + (size_t)next_pow2(K) * 8 + 2 * BS * 8 + (size_t)P * 8 + sizeof(BlockShared) +
+         2 * sizeof(int) + 2 * (size_t)P;
 }
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st) {

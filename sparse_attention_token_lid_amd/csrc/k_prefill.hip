@@ -134,85 +134,129 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   WaveTopK st;
   wave_topk_init(st, cand + (size_t)wv * a.cap, hist + wv * 256, a.K, a.cap);
 
-  // cooperative global -> LDS copy of one key tile (16-byte chunks, XOR-swizzled)
-  constexpr int PER_T = kChunksPerTile / (NW * 64);
-  static_assert(PER_T * NW * 64 == kChunksPerTile, "tile copy must divide evenly");
-  u32x4 stage[PER_T];
+  // Key tiles go straight from global memory to LDS (global_load_lds_dwordx4:
+  // each lane's 16 bytes land at LDS base + 16 * lane, so one instruction
+  // fills 1 KiB = 4 rows).  The XOR swizzle of the LDS layout is applied by
+  // permuting which 16-byte chunk each lane fetches.  Rows past n_kv are
+  // clamped to the last key (never scored), so the loads need no branches.
+  constexpr int kInstPerTile = kTileBytes / 1024;           // 16
+  constexpr int kInstPerWave = kInstPerTile / NW;
+  static_assert(kInstPerWave * NW == kInstPerTile, "tile copy must divide evenly");
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
-  auto gload = [&](int64_t tile) {
+  const int64_t last_key = a.n_kv - 1;
+  auto gload = [&](int64_t tile, int buf) {
 #pragma unroll
-    for (int r = 0; r < PER_T; ++r) {
-      int c = threadIdx.x + r * NW * 64;
-      int row = c >> 4, ch = c & 15;
+    for (int r = 0; r < kInstPerWave; ++r) {
+      const int q = wv * kInstPerWave + r;          // 1 KiB piece of the tile
+      const int row = 4 * q + (lane >> 4);
+      const int ch = (lane & 15) ^ (row & 15);
       int64_t s = tile * TN + row;
-      u32x4 v = {0, 0, 0, 0};
-      if (s < a.n_kv) v = *reinterpret_cast<const u32x4*>(kbase + s * D + ch * 8);
-      stage[r] = v;
+      s = s < last_key ? s : last_key;
+      __builtin_amdgcn_global_load_lds(kbase + s * D + ch * 8, ktile + buf * TN * D + q * 512, 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  // this wave's mask values for one tile (lane l <-> key tile*64 + l); read one
+  // tile ahead so that no wait on global memory sits in front of the MFMAs
+  const bool wave_has_keys = has_q && whi > wlo;
+  const uint16_t* mrow = a.mask ? a.mask + (has_q ? t : 0) * a.mask_ld : nullptr;
+  auto mload = [&](int64_t tile) -> uint16_t {
+    if (!mrow || !wave_has_keys) return 0;
+    int64_t s = tile * TN + lane;
+    s = s < wlo ? wlo : (s >= whi ? whi - 1 : s);
+    return __builtin_nontemporal_load(mrow + s);
+  };
+
+  // Software pipeline over 32-key halves.  Step "A" of tile i issues the 16
+  // MFMAs of keys 0-31 while the VALU epilogue of tile i-1's keys 32-63 runs;
+  // then tile i-1's 64 scores enter the top-k; step "B" issues the MFMAs of
+  // keys 32-63 while the epilogue of keys 0-31 runs.  Neither half waits for
+  // its own MFMAs, so the matrix pipe stays busy during the epilogue.
+  // Head reduction of one 32-key half.  The summation order (four partial
+  // sums, combined as (s0 + s1) + (s2 + s3)) is the same here and inside
+  // step(), so a key's score does not depend on where its tile falls.
+  auto epilogue = [&](const f32x16 (&acc)[2]) -> float {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
-    for (int r = 0; r < PER_T; ++r) {
-      int c = threadIdx.x + r * NW * 64;
-      int row = c >> 4, ch = c & 15;
-      *reinterpret_cast<u32x4*>(ktile + buf * TN * D + swz(row, ch)) = stage[r];
+    for (int j = 0; j < 8; ++j) {
+      s0 = __builtin_fmaf(wr[0][2 * j], relu(acc[0][2 * j]), s0);
+      s1 = __builtin_fmaf(wr[1][2 * j], relu(acc[1][2 * j]), s1);
+      s2 = __builtin_fmaf(wr[0][2 * j + 1], relu(acc[0][2 * j + 1]), s2);
+      s3 = __builtin_fmaf(wr[1][2 * j + 1], relu(acc[1][2 * j + 1]), s3);
     }
+    return (s0 + s1) + (s2 + s3);
+  };
+  // One pipeline step: the 16 MFMAs of key half `kb` of tile `kt` into acc,
+  // with the epilogue of `prev` (the half scored one step earlier) spread
+  // between them, 4 VALU ops after each MFMA; B fragments are read from LDS
+  // two k-steps ahead.  The order is pinned with scheduling barriers.
+  auto step = [&](const uint16_t* kt, int kb, f32x16 (&acc)[2], const f32x16 (&prev)[2]) -> float {
+    const int row = 32 * kb + m;
+    auto frag = [&](int j) { return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + swz(row, 8 * g + j))); };
+    const f32x16 zero = {};
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    T bq[3];
+    bq[0] = frag(0);
+    bq[1] = frag(1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j + 2 < 8) bq[(j + 2) % 3] = frag(j + 2);
+      const T b = bq[j % 3];
+      // (the empty asm statements keep each group of epilogue ops next to its
+      // MFMA; without them instruction selection moves the whole epilogue
+      // behind the last MFMA)
+      acc[0] = M::run(A[0][j], b, j == 0 ? zero : acc[0]);
+      s0 = __builtin_fmaf(wr[0][2 * j], relu(prev[0][2 * j]), s0);
+      s1 = __builtin_fmaf(wr[1][2 * j], relu(prev[1][2 * j]), s1);
+      asm volatile("" : "+v"(s0), "+v"(s1));
+      __builtin_amdgcn_sched_barrier(0);
+      acc[1] = M::run(A[1][j], b, j == 0 ? zero : acc[1]);
+      s2 = __builtin_fmaf(wr[0][2 * j + 1], relu(prev[0][2 * j + 1]), s2);
+      s3 = __builtin_fmaf(wr[1][2 * j + 1], relu(prev[1][2 * j + 1]), s3);
+      asm volatile("" : "+v"(s2), "+v"(s3));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return (s0 + s1) + (s2 + s3);
+  };
+  auto insert_tile = [&](int64_t s0, float p0, float p1, uint16_t mb, bool live) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int64_t s = s0 + lane;
+    const float v = (tot + f16_bits_to_f32(mb)) + 0.0f;
+    const bool valid = live && s >= wlo && s < whi && v != -__builtin_inff();
+    wave_topk_insert(st, make_key(v, (uint32_t)s), valid);
   };
 
   const int64_t ntile = c1 - c0;
+  uint16_t mbits = 0;
   if (ntile > 0) {
-    gload(c0);
-    sstore(0);
+    mbits = mload(c0);
+    gload(c0, 0);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 accA[2], accB[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) { accB[0][e] = 0.f; accB[1][e] = 0.f; }
+  float part0 = 0.f;
+  uint16_t mprev = 0;
   for (int64_t it = 0; it < ntile; ++it) {
     const int64_t tile = c0 + it;
-    const int cur = (int)(it & 1);
-    if (it + 1 < ntile) gload(tile + 1);
-    const int64_t s0 = tile * TN;
-    if (has_q && s0 < whi && s0 + TN > wlo) {
-      const int64_t s = s0 + lane;
-      const bool inr = s >= wlo && s < whi;
-      float mv = 0.f;
-      if (a.mask && inr) mv = f16_bits_to_f32(a.mask[t * a.mask_ld + s]);
-      f32x16 acc[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[kb][rb][e] = 0.f;
-      const uint16_t* kt = ktile + cur * TN * D;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = 32 * kb + m;
-          T b = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + swz(row, 8 * g + j)));
-          acc[kb][0] = M::run(A[0][j], b, acc[kb][0]);
-          acc[kb][1] = M::run(A[1][j], b, acc[kb][1]);
-        }
-      }
-      float part[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float sum = 0.f;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sum = __builtin_fmaf(wr[rb][e], __builtin_fmaxf(acc[kb][rb][e], 0.f), sum);
-        part[kb] = sum;
-      }
-      // lanes 0-31: key half 0 (both head halves summed), lanes 32-63: key half 1
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
-      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      const float v = (tot + mv) + 0.0f;
-      const bool valid = inr && v != -__builtin_inff();
-      wave_topk_insert(st, make_key(v, (uint32_t)s), valid);
+    const uint16_t* kt = ktile + (int)(it & 1) * TN * D;
+    const uint16_t mcur = mbits;
+    if (it + 1 < ntile) {
+      mbits = mload(tile + 1);
+      gload(tile + 1, (int)((it + 1) & 1));
     }
-    if (it + 1 < ntile) sstore(cur ^ 1);
+    // step A: MFMAs of keys 0-31 of this tile || epilogue of keys 32-63 of the previous tile
+    const float part1 = step(kt, 0, accA, accB);
+    insert_tile((tile - 1) * TN, part0, part1, mprev, it > 0);
+    // step B: MFMAs of keys 32-63 || epilogue of keys 0-31
+    part0 = step(kt, 1, accB, accA);
+    mprev = mcur;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's part of the next tile has landed in LDS
     __syncthreads();
   }
+  if (ntile > 0) insert_tile((c1 - 1) * TN, part0, epilogue(accB), mprev, true);
 
   if (has_q) {
     wave_topk_finish(st);

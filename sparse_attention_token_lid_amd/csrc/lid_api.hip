@@ -15,7 +15,8 @@ using namespace lid;
 constexpr int kMaxTopK = 1024;
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeMaxTok = 4;       // auto plan: at most this many queries use the decode kernel
-constexpr int kDecodeKeysPerSplit = 1024;
+constexpr int kDecodeKeysPerSplit = 256;
+constexpr int64_t kCUs = 256;          // MI355X compute units
 constexpr int kDecodeMaxSplits = 256;  // bounds the decode workspace independently of n_kv
 constexpr size_t kMaxLds = 160 * 1024;
 
@@ -85,8 +86,13 @@ int make_plan(const lid_shape* s, Plan* pl) {
     const int64_t tiles = cdiv(s->n_kv, kPrefillTile);
     int P = s->splits;
     if (!P) {
+      // enough (query block, split) workgroups for one per CU, but never a
+      // split shorter than 32 tiles (2048 keys)
       const int64_t nqb = cdiv(s->n_tok, pl->nw);
-      P = (nqb >= 1024 || tiles < 64) ? 1 : 8;
+      int64_t want = cdiv(kCUs, nqb);
+      const int64_t cap = tiles / 32 > 1 ? tiles / 32 : 1;
+      want = want < cap ? want : cap;
+      P = (int)(want < 1 ? 1 : (want > 64 ? 64 : want));
     }
     pl->P = P;
     if (prefill_lds_bytes(pl->nw, pl->cap) > kMaxLds) return LID_ERR_UNSUPPORTED;

@@ -38,6 +38,11 @@ __device__ __forceinline__ float key_score(uint64_t key) {
   return key ? unord_f32((uint32_t)(key >> 32)) : -__builtin_inff();
 }
 
+// max(x, 0) for finite x as one v_med3_f32 (clamp to [0, FLT_MAX]); fmaxf
+// (or a med3 against +inf, which the compiler folds back into fmaxf) would add
+// a NaN-quieting canonicalisation of every MFMA result first.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
+
 // f16 mask bits -> f32 (exact)
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   _Float16 x = __builtin_bit_cast(_Float16, h);
@@ -54,32 +59,76 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
-  uint32_t lo = __shfl_xor((uint32_t)x, mask);
-  uint32_t hi = __shfl_xor((uint32_t)(x >> 32), mask);
-  return ((uint64_t)hi << 32) | lo;
+// Partner value of this lane's x in the xor-J butterfly (J < 64), with
+// VALU-only exchanges: DPP quad_perm (xor 1, 2), row_shl/row_shr (xor 4),
+// row_ror:8 (xor 8), v_permlane16_swap (xor 16), v_permlane32_swap (xor 32).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x) {
+  const int L = lane_id();
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x104, 0xF, 0xF, true);  // row_shl:4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    return (L & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);  // row_ror:8
+  } else if constexpr (J == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (L & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "xor distance");
+    auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (L & 32) ? r[0] : r[1];
+  }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x) {
+  return ((uint64_t)xor_lane_u32<J>((uint32_t)(x >> 32)) << 32) | xor_lane_u32<J>((uint32_t)x);
+}
+
+// Butterfly reductions over the 64 lanes (every lane gets the result).
+template <typename Op>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t x, Op op) {
+  x = op(x, xor_lane_u64<1>(x));
+  x = op(x, xor_lane_u64<2>(x));
+  x = op(x, xor_lane_u64<4>(x));
+  x = op(x, xor_lane_u64<8>(x));
+  x = op(x, xor_lane_u64<16>(x));
+  x = op(x, xor_lane_u64<32>(x));
+  return x;
 }
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t y = shfl_xor_u64(x, o);
-    x = y < x ? y : x;
-  }
-  return x;
+  return wave_reduce_u64(x, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ uint64_t wave_and_u64(uint64_t x) {
-  for (int o = 32; o > 0; o >>= 1) x &= shfl_xor_u64(x, o);
-  return x;
+  return wave_reduce_u64(x, [](uint64_t a, uint64_t b) { return a & b; });
 }
 __device__ __forceinline__ uint64_t wave_or_u64(uint64_t x) {
-  for (int o = 32; o > 0; o >>= 1) x |= shfl_xor_u64(x, o);
+  return wave_reduce_u64(x, [](uint64_t a, uint64_t b) { return a | b; });
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  x += xor_lane_u32<1>(x);
+  x += xor_lane_u32<2>(x);
+  x += xor_lane_u32<4>(x);
+  x += xor_lane_u32<8>(x);
+  x += xor_lane_u32<16>(x);
+  x += xor_lane_u32<32>(x);
   return x;
 }
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (no LDS traffic): within each row of 16 lanes, then rows 0-1
+// into row 1 / rows 2-3 into row 3 (row_bcast:15), then rows 0-1 into 2-3.
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
-  const int lane = lane_id();
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return x;
 }
 
@@ -109,9 +158,9 @@ __device__ __forceinline__ DigitPick pick_digit(const uint32_t* hist, uint32_t n
     else if (a + c0 + c1 + c2 >= need) { d = 253 - 4 * lane; above = a + c0 + c1; cnt = c2; }
     else                           { d = 252 - 4 * lane; above = a + c0 + c1 + c2; cnt = c3; }
   }
-  r.d = __shfl(d, fl);
-  r.above = __shfl(above, fl);
-  r.cnt = __shfl(cnt, fl);
+  r.d = (uint32_t)__builtin_amdgcn_readlane((int)d, fl);
+  r.above = (uint32_t)__builtin_amdgcn_readlane((int)above, fl);
+  r.cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, fl);
   return r;
 }
 
@@ -264,116 +313,80 @@ __device__ inline void wave_write_row(const uint64_t* buf, int K, int32_t* idx_r
 }
 
 // ------------------------------------------------------------ block-wide ops
-// All threads of the block call these (blockDim.x = BS, a multiple of 64).
+// All threads of the block call these (blockDim.x = BS, a multiple of 64,
+// 128 <= BS <= 1024).  Barriers are the expensive part, so each helper uses
+// as few as it can.
 
 struct BlockShared {
-  uint32_t hist[256];
-  uint32_t wcount[16];
+  uint32_t hist[3][256];  // radix histograms (triple buffered)
+  int32_t wsum[16];       // per-wavefront partial sums
   uint64_t red_and, red_or, red_min;
   uint32_t nz;
   uint32_t pick_d, pick_above, pick_cnt;
 };
 
-// Number of nonzero keys in arr[0..n).
-__device__ inline uint32_t block_count_nonzero(const uint64_t* arr, int n, BlockShared& sh) {
-  if (threadIdx.x == 0) sh.nz = 0;
+// Exclusive prefix sum of one int per thread over the block; *total gets the sum.
+__device__ inline int block_excl_scan(int x, int* total, BlockShared& sh) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int incl = (int)wave_incl_scan_u32((uint32_t)x);
+  if (lane == kWave - 1) sh.wsum[wv] = incl;
   __syncthreads();
-  uint32_t c = 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) c += arr[i] != 0ull;
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-  if (lane_id() == 0) atomicAdd(&sh.nz, c);
+  int base = 0, tot = 0;
+  for (int w2 = 0; w2 < nw; ++w2) {
+    const int c = sh.wsum[w2];
+    base += (w2 < wv) ? c : 0;
+    tot += c;
+  }
   __syncthreads();
-  uint32_t r = sh.nz;
-  __syncthreads();
-  return r;
+  *total = tot;
+  return base + incl - x;
 }
 
-// K-th largest among the nonzero keys of arr[0..n) (requires K <= nonzero count).
-__device__ inline uint64_t block_kth_largest(const uint64_t* arr, int n, int K, BlockShared& sh) {
-  const int lane = lane_id();
-  if (threadIdx.x == 0) { sh.red_and = ~0ull; sh.red_or = 0ull; sh.red_min = ~0ull; }
-  __syncthreads();
-  uint64_t a = ~0ull, o = 0ull;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    uint64_t e = arr[i];
-    if (e) { a &= e; o |= e; }
+// One compare-exchange stage (k, j) of a descending bitonic sort with one
+// element per thread; partners in other wavefronts (j >= 64) meet in LDS
+// (ping-pong halves of tmp, one barrier per stage).
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t& x, uint64_t* tmp, int& flip) {
+  const int i = threadIdx.x;
+  uint64_t y;
+  if constexpr (J >= kWave) {
+    uint64_t* t = tmp + flip * blockDim.x;
+    flip ^= 1;
+    t[i] = x;
+    __syncthreads();
+    y = t[i ^ J];
+  } else {
+    y = xor_lane_u64<J>(x);
   }
-  a = wave_and_u64(a);
-  o = wave_or_u64(o);
-  if (lane == 0) { atomicAnd((unsigned long long*)&sh.red_and, a); atomicOr((unsigned long long*)&sh.red_or, o); }
-  __syncthreads();
-  a = sh.red_and;
-  o = sh.red_or;
-  uint64_t diff = a ^ o;
-  if (diff == 0ull) { __syncthreads(); return a; }
-  int top = 63 - __clzll((long long)diff);
-  uint64_t pmask = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
-  uint64_t prefix = a & pmask;
-  uint32_t need = (uint32_t)K;
-  int shift = top - 7;
-  for (;;) {
-    int sh8 = shift > 0 ? shift : 0;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[i] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      uint64_t e = arr[i];
-      if (e && (e & pmask) == prefix) atomicAdd(&sh.hist[(uint32_t)(e >> sh8) & 0xFFu], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      DigitPick p = pick_digit(sh.hist, need);
-      if (threadIdx.x == 0) { sh.pick_d = p.d; sh.pick_above = p.above; sh.pick_cnt = p.cnt; }
-    }
-    __syncthreads();
-    uint32_t d = sh.pick_d, above = sh.pick_above, cnt = sh.pick_cnt;
-    __syncthreads();
-    need -= above;
-    prefix |= (uint64_t)d << sh8;
-    pmask |= 0xFFull << sh8;
-    if (cnt == need || sh8 == 0) break;
-    shift -= 8;
-  }
-  uint64_t mn = ~0ull;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    uint64_t e = arr[i];
-    if (e >= prefix && e < mn) mn = e;
-  }
-  mn = wave_min_u64(mn);
-  if (lane == 0) atomicMin((unsigned long long*)&sh.red_min, mn);
-  __syncthreads();
-  uint64_t r = sh.red_min;
-  __syncthreads();
-  return r;
+  const bool take_max = ((i & K) == 0) == ((i & J) == 0);
+  x = (take_max == (x > y)) ? x : y;
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge_steps(uint64_t& x, uint64_t* tmp, int& flip) {
+  bitonic_stage<K, J>(x, tmp, flip);
+  if constexpr (J > 1) bitonic_merge_steps<K, J / 2>(x, tmp, flip);
+}
+template <int N2, int K = 2>
+__device__ __forceinline__ void bitonic_all(uint64_t& x, uint64_t* tmp, int& flip) {
+  bitonic_merge_steps<K, K / 2>(x, tmp, flip);
+  if constexpr (K < N2) bitonic_all<N2, K * 2>(x, tmp, flip);
 }
 
-// Copy the keys of src[0..n) that are >= kappa (and nonzero) to dst[0..),
-// keeping their order; returns the number copied.  src and dst must not overlap.
-__device__ inline int block_compact(const uint64_t* src, int n, uint64_t kappa, uint64_t* dst, BlockShared& sh) {
-  const int wv = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  int base = 0;
-  for (int i0 = 0; i0 < n; i0 += blockDim.x) {
-    int i = i0 + threadIdx.x;
-    uint64_t e = (i < n) ? src[i] : 0ull;
-    bool keep = (i < n) && e != 0ull && e >= kappa;
-    uint64_t m = ballot(keep);
-    if (lane_id() == 0) sh.wcount[wv] = __popcll(m);
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w2 = 0; w2 < nw; ++w2) {
-      int c = sh.wcount[w2];
-      before += (w2 < wv) ? c : 0;
-      total += c;
-    }
-    if (keep) dst[base + before + mbcnt(m)] = e;
-    base += total;
-    __syncthreads();
-  }
-  return base;
+// Bitonic sort of buf[0..N2) descending (N2 a power of two <= blockDim.x),
+// fully unrolled; tmp holds 2 * blockDim.x entries.
+template <int N2>
+__device__ inline void block_sort_desc_n(uint64_t* buf, uint64_t* tmp) {
+  const int i = threadIdx.x;
+  uint64_t x = (i < N2) ? buf[i] : 0ull;
+  int flip = 0;
+  if constexpr (N2 > 1) bitonic_all<N2>(x, tmp, flip);
+  __syncthreads();
+  if (i < N2) buf[i] = x;
+  __syncthreads();
 }
 
-// Bitonic sort of buf[0..n2) descending, whole block.
-__device__ inline void block_sort_desc(uint64_t* buf, int n2) {
+// Bitonic sort through LDS only (any n2 <= 2048), for sizes beyond blockDim.
+__device__ inline void block_sort_desc_lds(uint64_t* buf, int n2) {
   for (int k = 2; k <= n2; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < (n2 >> 1); i += blockDim.x) {
@@ -388,17 +401,130 @@ __device__ inline void block_sort_desc(uint64_t* buf, int n2) {
   }
 }
 
-// Select the K best nonzero keys of arr[0..n) into sel[0..K) sorted
-// descending, padded with empty keys (sel has room for next_pow2(K)).
-__device__ inline void block_select_sorted(const uint64_t* arr, int n, int K, uint64_t* sel, BlockShared& sh) {
-  uint32_t nz = block_count_nonzero(arr, n, sh);
+// K-th largest among the nonzero keys of arr[0..n) (all nonzero keys unique);
+// needs K <= nonzero count.  Starts at the highest bit where keys differ
+// (a, o = AND / OR of the nonzero keys) and resolves 8 bits per pass.  Every
+// wavefront reads the histogram and picks the digit itself, and the three
+// histogram buffers rotate (pass p fills buffer p % 3 and clears buffer
+// (p + 2) % 3, last read in pass p - 1), so one barrier per pass suffices.
+__device__ inline uint64_t block_kth_largest(const uint64_t* arr, int n, int K, uint64_t a, uint64_t o,
+                                             BlockShared& sh) {
+  const uint64_t diff = a ^ o;
+  if (diff == 0ull) return a;
+  const int top = 63 - __clzll((long long)diff);
+  uint64_t pmask = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
+  uint64_t prefix = a & pmask;
+  uint32_t need = (uint32_t)K;
+  int shift = top - 7;
+  for (int pass = 0;; ++pass) {
+    const int sh8 = shift > 0 ? shift : 0;
+    uint32_t* hist = sh.hist[pass % 3];
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint64_t e = arr[i];
+      if (e && (e & pmask) == prefix) atomicAdd(&hist[(uint32_t)(e >> sh8) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    const DigitPick pk = pick_digit(hist, need);
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) sh.hist[(pass + 2) % 3][i] = 0;
+    need -= pk.above;
+    prefix |= (uint64_t)pk.d << sh8;
+    pmask |= 0xFFull << sh8;
+    if (pk.cnt == need || sh8 == 0) break;
+    shift -= 8;
+  }
+  // every key >= prefix is selected (exactly K of them); the K-th is their minimum
+  uint64_t mn = ~0ull;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint64_t e = arr[i];
+    if (e >= prefix && e < mn) mn = e;
+  }
+  mn = wave_min_u64(mn);
+  if (lane_id() == 0) atomicMin((unsigned long long*)&sh.red_min, mn);
+  __syncthreads();
+  return sh.red_min;
+}
+
+// Copy the nonzero keys >= kappa of src[0..n) to dst[0..) in order (each
+// thread owns one contiguous slice); returns the count.  No overlap allowed.
+__device__ inline int block_compact(const uint64_t* src, int n, uint64_t kappa, uint64_t* dst, BlockShared& sh) {
+  const int per = (n + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int lo = threadIdx.x * per;
+  const int hi = lo + per < n ? lo + per : n;
+  int c = 0;
+  for (int i = lo; i < hi; ++i) {
+    const uint64_t e = src[i];
+    c += (e != 0ull && e >= kappa);
+  }
+  int total;
+  int pos = block_excl_scan(c, &total, sh);
+  for (int i = lo; i < hi; ++i) {
+    const uint64_t e = src[i];
+    if (e != 0ull && e >= kappa) dst[pos++] = e;
+  }
+  __syncthreads();
+  return total;
+}
+
+// AND / OR / count of the nonzero keys of arr[0..n); also zeroes the radix
+// histograms and the min slot for block_kth_largest.
+__device__ inline uint32_t block_key_stats(const uint64_t* arr, int n, uint64_t* a_out, uint64_t* o_out,
+                                           BlockShared& sh) {
+  if (threadIdx.x == 0) { sh.red_and = ~0ull; sh.red_or = 0ull; sh.red_min = ~0ull; sh.nz = 0; }
+  for (int i = threadIdx.x; i < 3 * 256; i += blockDim.x) (&sh.hist[0][0])[i] = 0;
+  __syncthreads();
+  uint64_t a = ~0ull, o = 0ull;
+  uint32_t c = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint64_t e = arr[i];
+    if (e) { a &= e; o |= e; ++c; }
+  }
+  a = wave_and_u64(a);
+  o = wave_or_u64(o);
+  c = wave_sum_u32(c);
+  if (lane_id() == 0) {
+    atomicAnd((unsigned long long*)&sh.red_and, a);
+    atomicOr((unsigned long long*)&sh.red_or, o);
+    atomicAdd(&sh.nz, c);
+  }
+  __syncthreads();
+  *a_out = sh.red_and;
+  *o_out = sh.red_or;
+  return sh.nz;
+}
+
+// Descending sort of buf[0..n2) for a power of two n2 <= 1024: the unrolled
+// register network when n2 <= blockDim.x, else the LDS network.
+__device__ inline void block_sort_desc(uint64_t* buf, int n2, uint64_t* tmp) {
+  if (n2 > (int)blockDim.x) { block_sort_desc_lds(buf, n2); return; }
+  switch (n2) {
+    case 1: break;
+    case 2: block_sort_desc_n<2>(buf, tmp); break;
+    case 4: block_sort_desc_n<4>(buf, tmp); break;
+    case 8: block_sort_desc_n<8>(buf, tmp); break;
+    case 16: block_sort_desc_n<16>(buf, tmp); break;
+    case 32: block_sort_desc_n<32>(buf, tmp); break;
+    case 64: block_sort_desc_n<64>(buf, tmp); break;
+    case 128: block_sort_desc_n<128>(buf, tmp); break;
+    case 256: block_sort_desc_n<256>(buf, tmp); break;
+    case 512: block_sort_desc_n<512>(buf, tmp); break;
+    default: block_sort_desc_n<1024>(buf, tmp); break;
+  }
+}
+
+// The K best nonzero keys of arr[0..n) into sel[0..K), sorted descending and
+// padded with empty keys; sel has room for next_pow2(K) entries, tmp for
+// 2 * blockDim.x.  sel must not overlap arr.
+__device__ inline void block_select_sorted(const uint64_t* arr, int n, int K, uint64_t* sel, uint64_t* tmp,
+                                           BlockShared& sh) {
+  uint64_t a, o;
+  const uint32_t nz = block_key_stats(arr, n, &a, &o, sh);
   uint64_t kappa = 1ull;
-  if ((int)nz > K) kappa = block_kth_largest(arr, n, K, sh);
-  int m = block_compact(arr, n, kappa, sel, sh);
+  if ((int)nz > K) kappa = block_kth_largest(arr, n, K, a, o, sh);
+  const int m = block_compact(arr, n, kappa, sel, sh);
   const int n2 = next_pow2(K);
   for (int i = m + threadIdx.x; i < n2; i += blockDim.x) sel[i] = 0ull;
   __syncthreads();
-  block_sort_desc(sel, n2);
+  block_sort_desc(sel, n2, tmp);
 }
 
 }  // namespace lid

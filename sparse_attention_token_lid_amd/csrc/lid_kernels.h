@@ -26,7 +26,7 @@ struct KArgs {
 constexpr int kMfmaHeads = 64;
 constexpr int kMfmaDim = 128;
 constexpr int kPrefillTile = 64;       // keys per LDS tile
-constexpr int kDecodeMaxKeys = 16384;  // keys one decode workgroup scores (LDS bound)
+constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);
