@@ -87,15 +87,17 @@ int make_plan(const lid_shape* s, Plan* pl) {
     int P = s->splits;
     if (!P) {
       // enough (query block, split) workgroups for one per CU, but never a
-      // split shorter than 32 tiles (2048 keys)
+      // split shorter than 2048 keys
       const int64_t nqb = cdiv(s->n_tok, pl->nw);
       int64_t want = cdiv(kCUs, nqb);
-      const int64_t cap = tiles / 32 > 1 ? tiles / 32 : 1;
+      const int64_t min_tiles = 2048 / kPrefillTile;
+      const int64_t cap = tiles / min_tiles > 1 ? tiles / min_tiles : 1;
       want = want < cap ? want : cap;
       P = (int)(want < 1 ? 1 : (want > 64 ? 64 : want));
     }
     pl->P = P;
-    if (prefill_lds_bytes(pl->nw, pl->cap) > kMaxLds) return LID_ERR_UNSUPPORTED;
+    if (prefill_lds_bytes(pl->nw, pl->cap) + 2 * (size_t)kPrefillTile * kMfmaDim * 2 > kMaxLds)
+      return LID_ERR_UNSUPPORTED;
   } else {  // decode
     int P = s->splits;
     if (!P) {

@@ -235,10 +235,12 @@ struct WaveTopK {
   int K;
   int cap;
   uint64_t tau;    // insert iff key > tau
+  float tau_v;     // score part of tau (-inf while tau == 0): v < tau_v can never enter
 };
 
 __device__ __forceinline__ void wave_topk_init(WaveTopK& st, uint64_t* buf, uint32_t* hist, int K, int cap) {
   st.buf = buf; st.hist = hist; st.count = 0; st.K = K; st.cap = cap; st.tau = 0ull;
+  st.tau_v = -__builtin_inff();
 }
 
 __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
@@ -246,6 +248,7 @@ __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
     uint64_t kap = wave_kth_largest(st.buf, st.count, st.K, st.hist);
     st.count = wave_compact(st.buf, st.count, kap);
     st.tau = kap;
+    st.tau_v = key_score(kap);
   }
 }
 

@@ -25,7 +25,7 @@ struct KArgs {
 // Shapes the MFMA kernels are written for.
 constexpr int kMfmaHeads = 64;
 constexpr int kMfmaDim = 128;
-constexpr int kPrefillTile = 64;       // keys per LDS tile
+constexpr int kPrefillTile = 128;      // keys per LDS tile
 constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
 
 // Launchers (return hipSuccess or the launch error).
