@@ -14,16 +14,18 @@
 // per workgroup and shared by its NW wavefronts (double buffered, one barrier
 // per tile).
 //
-// Per wavefront and 32-key half of a tile: S = Q_t (64 heads x 128) . K^T with
-// v_mfma_f32_32x32x16 (f16 or bf16 in, f32 accumulate): 2 row blocks of 32
-// heads x 8 k-steps.  Heads run along the MFMA
-// rows, so each lane holds 16 heads of one key and the head reduction
-// sum_h w_h * max(S_h, 0) is 32 fused multiply-adds in registers plus one
-// permlane32 swap that also turns the two 32-key halves into one 64-lane
-// vector (lane l <-> key tile_base + l).
+// Per wavefront and 16-key block of a tile: S = Q_t (64 heads x 128) . K^T
+// with v_mfma_f32_16x16x32 (f16 or bf16 in, f32 accumulate): 4 row blocks of
+// 16 heads x 4 k-steps.  Heads run along the MFMA rows, so each lane holds 16
+// heads of one key, and the head reduction sum_h w_h * max(S_h, 0) is 16
+// fused multiply-adds in registers per block; the four lane groups of a block
+// are summed by three permlane swaps per 64 keys, which also leave key
+// s0 + l of a 64-key unit in lane l.  On gfx950 this MFMA shape runs at a
+// higher sustained clock than 32x32x16 under the same data (the chip is power
+// limited here), which is why the kernel uses it.
 //
 // The k-index of the MFMA is mapped to the head dimension as
-// d = 64 * (lane / 32) + 8 * kstep + i, so each lane's 8 k-steps cover 128
+// d = 32 * (lane / 16) + 8 * kstep + i, so each lane's 4 k-steps cover 64
 // contiguous bytes of a q or k row.
 #include "lid_device.h"
 #include "lid_kernels.h"
@@ -32,33 +34,55 @@ namespace lid {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <int DT> struct Mfma;
 template <> struct Mfma<1> {
   typedef f16x8 T;
-  static __device__ __forceinline__ f32x16 run(T a, T b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ f32x4 run(T a, T b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 template <> struct Mfma<2> {
   typedef bf16x8 T;
-  static __device__ __forceinline__ f32x16 run(T a, T b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  static __device__ __forceinline__ f32x4 run(T a, T b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
 
 constexpr int H = kMfmaHeads;
 constexpr int D = kMfmaDim;
-constexpr int TN = kPrefillTile;              // keys per tile (4 halves of 32)
+constexpr int TN = kPrefillTile;              // keys per tile (8 blocks of 16)
 constexpr int kTileBytes = TN * D * 2;         // 32 KiB
-constexpr int kHalfBytes = 32 * D * 2;         // 8 KiB
+constexpr int kBlockBytes = 16 * D * 2;        // 4 KiB
 
-__device__ __forceinline__ int swz(int row, int ch) { return row * D + ((ch ^ (row & 15)) << 3); }
+// One global_load_lds_dwordx4: lane l copies 16 bytes from gbase + voff into
+// LDS byte address lds_addr + 16 l (lds_addr wave-uniform).  M0, which
+// carries the LDS address, is saved and restored around it.  The caller waits
+// for completion with s_waitcnt vmcnt(0).
+__device__ __forceinline__ void dma_row4(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
 
-template <int NW, int DT>
+// out[lane] = bit lane of m ? a : b (one v_cndmask_b32 on a scalar lane mask)
+__device__ __forceinline__ float lane_select(uint64_t m, float a, float b) {
+  float r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
+}
+
+template <int NW, int DT, bool MK>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   using M = Mfma<DT>;
   using T = typename M::T;
@@ -73,9 +97,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   int64_t* rlo = reinterpret_cast<int64_t*>(hist + NW * 256);
   int64_t* rhi = rlo + NW;
 
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
-  const int g = lane >> 5, m = lane & 31;
+  const int G = lane >> 4, r16 = lane & 15;
   const int P = a.P;
   const int p = (int)(blockIdx.x % (unsigned)P);
   const int64_t qb = blockIdx.x / (unsigned)P;
@@ -111,58 +135,79 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // this wave's visible keys inside the chunk (32-bit: n_kv < 2^31)
   const int wlo = (int)(lo > (int64_t)c0 * TN ? lo : (int64_t)c0 * TN);
   const int whi = (int)(hi < (int64_t)c1 * TN ? hi : (int64_t)c1 * TN);
+  const uint32_t wspan = whi > wlo ? (uint32_t)(whi - wlo) : 0u;  // empty if the chunk misses the range
 
-  // this wave's query in MFMA A-operand layout, and its head weights
-  T A[2][8];
-  float wr[2][16];
+  // this wave's query in MFMA A-operand layout (A[rb][j]: head 16 rb + lane % 16,
+  // dims 32 (lane / 16) + 8 j ... + 7) and the weights of the heads its
+  // accumulators hold (wr[rb][e]: head 16 rb + 4 (lane / 16) + e)
+  T A[4][4];
+  float wr[4][4];
   {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (has_q ? t : 0) * H * D;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         u32x4 v = {0, 0, 0, 0};
-        if (has_q) v = *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j);
+        if (has_q) v = *reinterpret_cast<const u32x4*>(qrow + (16 * rb + r16) * D + 32 * G + 8 * j);
         A[rb][j] = __builtin_bit_cast(T, v);
       }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        int h = 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3);
-        wr[rb][jj] = has_q ? a.w[t * H + h] : 0.f;
-      }
+      for (int e = 0; e < 4; ++e) wr[rb][e] = has_q ? a.w[t * H + 16 * rb + 4 * G + e] : 0.f;
   }
 
+  // Streaming top-k state.  Scores enter on an f32 test alone (v >= tau_v,
+  // where tau_v is the score of the k_top-th best key at the last
+  // compaction): every key that beats tau passes it, and the few that tie
+  // tau_v without beating tau only take buffer space until the next
+  // compaction.  tau_v starts at -FLT_MAX, so masked keys (-inf) never enter.
   WaveTopK st;
   wave_topk_init(st, cand + (size_t)wv * a.cap, hist + wv * 256, a.K, a.cap);
+  st.tau_v = -3.402823466e38f;
 
   // Key tiles go straight from global memory to LDS (global_load_lds_dwordx4:
   // each lane's 16 bytes land at LDS base + 16 * lane, so one instruction
   // fills 1 KiB = 4 rows).  The XOR swizzle of the LDS layout is applied by
-  // permuting which 16-byte chunk each lane fetches.  Rows past n_kv (only in
-  // the last tile) are clamped to the last key; they are never scored.
+  // permuting which 16-byte chunk each lane fetches; the per-lane byte offsets
+  // inside a tile are fixed, so a load is a scalar tile base plus one of them.
+  // Rows past n_kv (only in the last tile) are clamped to the last key; they
+  // are never scored.  The copy is issued through dma_row4() (inline asm):
+  // when the compiler sees an LDS DMA in flight it stops counting outstanding
+  // LDS reads and waits for all of them before every fragment use, so the
+  // copy is kept out of its view and waited for explicitly (vmcnt(0) before
+  // the barrier that ends a tile).
   constexpr int kInstPerWave = kTileBytes / 1024 / NW;
   static_assert(kInstPerWave * NW * 1024 == kTileBytes, "tile copy must divide evenly");
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(a.k);
   const int n_kv = (int)a.n_kv;
-  auto gload = [&](int tile, int buf) {
-    const bool tail = (tile + 1) * TN > n_kv;
+  uint32_t goff[kInstPerWave];
 #pragma unroll
-    for (int r = 0; r < kInstPerWave; ++r) {
-      const int q = wv * kInstPerWave + r;          // 1 KiB piece of the tile
-      const int row = 4 * q + (lane >> 4);
-      const int ch = (lane & 15) ^ (row & 15);
-      int s = tile * TN + row;
-      if (tail) s = s < n_kv - 1 ? s : n_kv - 1;
-      uint16_t* dst = (buf ? ktile1 : ktile0) + q * 512;
-      __builtin_amdgcn_global_load_lds(kbase + (size_t)s * D + ch * 8, dst, 16, 0, 0);
+  for (int r = 0; r < kInstPerWave; ++r) {
+    const int row = 4 * (wv * kInstPerWave + r) + (lane >> 4);
+    goff[r] = (uint32_t)(row * (D * 2) + (((lane & 15) ^ (row & 15)) << 4));
+  }
+  auto gload = [&](int tile, int buf) {
+    const unsigned char* tb = kbytes + (size_t)tile * kTileBytes;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((buf ? ktile1 : ktile0) + wv * kInstPerWave * 512);
+    if ((tile + 1) * TN <= n_kv) {
+#pragma unroll
+      for (int r = 0; r < kInstPerWave; ++r) dma_row4(tb, goff[r], lds0 + 1024 * r);
+    } else {
+      const int last = n_kv - 1 - tile * TN;  // last valid row of the tile
+#pragma unroll
+      for (int r = 0; r < kInstPerWave; ++r) {
+        const int row = (int)(goff[r] >> 8);
+        const uint32_t off = row <= last ? goff[r] : goff[r] - (uint32_t)((row - last) * (D * 2));
+        dma_row4(tb, off, lds0 + 1024 * r);
+      }
     }
   };
   // this wave's mask values for 64 keys (lane l <-> key s0 + l), read one
   // tile ahead so that no wait on global memory sits in front of the MFMAs
   const bool wave_has_keys = has_q && whi > wlo;
-  const uint16_t* mrow = (a.mask && wave_has_keys) ? a.mask + t * a.mask_ld : nullptr;
+  const uint16_t* mrow = (MK && wave_has_keys) ? a.mask + t * a.mask_ld : nullptr;
   auto mload = [&](int s0) -> uint16_t {
     if (!mrow) return 0;
     int s = s0 + lane;
@@ -170,68 +215,137 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     return __builtin_nontemporal_load(mrow + s);
   };
 
-  // LDS byte offset of B fragment j for this lane inside a 32-key half
-  uint32_t foff[8];
+  // LDS byte offset of B fragment j (key row lane % 16 of a block, dims
+  // 32 (lane / 16) + 8 j ... + 7) inside a 16-key block
+  uint32_t foff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) foff[j] = (uint32_t)(m * (D * 2) + (((8 * g + j) ^ (m & 15)) << 4));
+  for (int j = 0; j < 4; ++j) foff[j] = (uint32_t)(r16 * (D * 2) + (((4 * G + j) ^ r16) << 4));
+  auto frags = [&](int buf, int blk, T (&bq)[4]) {
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(buf ? ktile1 : ktile0) + blk * kBlockBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bq[j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + foff[j]));
+  };
 
-  // Head reduction of one 32-key half.  The summation order (four partial
-  // sums, combined as (s0 + s1) + (s2 + s3)) is the same here and inside
-  // step(), so a key's score does not depend on where its tile falls.
-  auto epilogue = [&](const f32x16 (&acc)[2]) -> float {
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  // Head reduction of one 16-key block, this lane's 16 heads, as one chain
+  // of fused multiply-adds in element order i = 4 rb + e (16 cycles apart in
+  // step(), so the chain never waits).  step() below uses the same order, so
+  // a key's score does not depend on where its block falls.  The chain starts
+  // from +0 and every term is added with round-to-nearest, so a zero sum is
+  // +0, never -0.
+  auto epilogue = [&](const f32x4 (&acc)[4]) -> float {
+    float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s0 = __builtin_fmaf(wr[0][2 * j], relu(acc[0][2 * j]), s0);
-      s1 = __builtin_fmaf(wr[1][2 * j], relu(acc[1][2 * j]), s1);
-      s2 = __builtin_fmaf(wr[0][2 * j + 1], relu(acc[0][2 * j + 1]), s2);
-      s3 = __builtin_fmaf(wr[1][2 * j + 1], relu(acc[1][2 * j + 1]), s3);
-    }
-    return (s0 + s1) + (s2 + s3);
+    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wr[i >> 2][i & 3], relu(acc[i >> 2][i & 3]), s);
+    return s;
   };
-  // One pipeline step: the 16 MFMAs of half `hq` of the tile in LDS buffer
-  // `buf` into acc, with the epilogue of `prev` (the half scored one step
-  // earlier) spread between them, 4 VALU ops after each MFMA; B fragments are
-  // read from LDS two k-steps ahead.  The order is pinned with scheduling
-  // barriers (the empty asm statements keep each group of epilogue ops next
-  // to its MFMA; without them instruction selection moves the whole epilogue
-  // behind the last MFMA).
-  auto step = [&](int buf, int hq, f32x16 (&acc)[2], const f32x16 (&prev)[2]) -> float {
-    const unsigned char* kt = reinterpret_cast<const unsigned char*>(buf ? ktile1 : ktile0) + hq * kHalfBytes;
-    auto frag = [&](int j) { return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + foff[j])); };
-    const f32x16 zero = {};
-    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    T bq[3];
-    bq[0] = frag(0);
-    bq[1] = frag(1);
+
+  // Hand-off of 64 finished keys (four 16-key blocks: this lane's partial
+  // sums p[0..3], unit base s0) to the top-k, done in slices between the
+  // MFMAs of the following step.  Two permlane32 swaps add lane groups {0,2}
+  // and {1,3}, one permlane16 swap adds the pairs, leaving key s0 + l in
+  // lane l.  Keys outside this wave's visible range are set to -inf with a
+  // lane mask built on the scalar unit; the rest pass on v >= tau_v.  If any
+  // lane passes, all 64 lanes store: passing keys at count + (rank among the
+  // passing lanes), the others at count + n + lane, past the new count, where
+  // they are dead (the buffer always has 128 free slots here: see room()).
+  // Adding the f16 mask to a sum that is never -0 cannot give -0 either, so
+  // v needs no further canonicalisation.
+  struct Unit {
+    float p[4];
+    int s0;
+    uint16_t mb;
+    bool live;
+  };
+  struct Slice {  // values carried between the slices of one hand-off
+    uint32_t x0, x1, y0, y1;
+    float v, mf;
+  };
+  auto insert_slice = [&](const Unit& u, int i, Slice& z) {
+    if (i == 0) {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u.p[0]), __float_as_uint(u.p[2]), false, false);
+      z.x0 = r[0]; z.x1 = r[1];
+      asm volatile("" : "+v"(z.x0), "+v"(z.x1));
+    } else if (i == 1) {
+      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u.p[1]), __float_as_uint(u.p[3]), false, false);
+      z.y0 = r[0]; z.y1 = r[1];
+      asm volatile("" : "+v"(z.y0), "+v"(z.y1));
+    } else if (i == 2) {
+      z.x0 = __float_as_uint(__uint_as_float(z.x0) + __uint_as_float(z.x1));
+      asm volatile("" : "+v"(z.x0));
+    } else if (i == 3) {
+      z.y0 = __float_as_uint(__uint_as_float(z.y0) + __uint_as_float(z.y1));
+      asm volatile("" : "+v"(z.y0));
+    } else if (i == 4) {
+      auto r = __builtin_amdgcn_permlane16_swap(z.x0, z.y0, false, false);
+      z.x0 = r[0]; z.x1 = r[1];
+      asm volatile("" : "+v"(z.x0), "+v"(z.x1));
+      if (MK) {
+        z.mf = f16_bits_to_f32(u.mb);
+        asm volatile("" : "+v"(z.mf));
+      }
+    } else if (i == 5) {
+      z.v = __uint_as_float(z.x0) + __uint_as_float(z.x1);
+      asm volatile("" : "+v"(z.v));
+    } else if (i == 6) {
+      if (MK) z.v = z.v + z.mf;
+      // lanes whose key lies outside [wlo, whi) (or all, for a dead unit)
+      const int l0 = wlo - u.s0, l1 = whi - u.s0;
+      const uint64_t below_hi = l1 >= kWave ? ~0ull : (l1 <= 0 ? 0ull : (1ull << l1) - 1);
+      const uint64_t below_lo = l0 >= kWave ? ~0ull : (l0 <= 0 ? 0ull : (1ull << l0) - 1);
+      const uint64_t inr = u.live ? (below_hi & ~below_lo) : 0ull;
+      z.v = lane_select(inr, z.v, -__builtin_inff());
+      asm volatile("" : "+v"(z.v));
+    } else if (i == 7) {
+      const bool pass = z.v >= st.tau_v;
+      const uint64_t m = ballot(pass);
+      if (m != 0ull) {
+        const uint32_t n = (uint32_t)__popcll(m);
+        const uint32_t c = (uint32_t)st.count;
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, c));
+        const uint32_t pos = pass ? rank : c + n + (uint32_t)lane;
+        const uint32_t b = __float_as_uint(z.v);
+        const uint32_t khi = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);  // ord_f32
+        const uint32_t klo = ~(uint32_t)(u.s0 + lane);
+        st.buf[pos] = ((uint64_t)khi << 32) | klo;
+        st.count += (int)n;
+      }
+    }
+  };
+  // Make room for one more unit: compaction to the k_top best when fewer than
+  // 128 free slots remain (rare once the stream is long).
+  auto room = [&]() {
+    if (st.count > st.cap - 2 * kWave) wave_topk_reduce(st);
+  };
+
+  // One pipeline step: the 16 MFMAs of the block whose B fragments are in bq
+  // into acc, with the head reduction of `prev` (the block scored one step
+  // earlier) spread between them, two VALU ops after each MFMA, the B
+  // fragments of the next block read from LDS into nxt (if load_next; all four
+  // behind the first MFMAs, so they have landed when the next step starts), and
+  // the slices of a pending top-k hand-off (if u is given).  The order is
+  // pinned with scheduling barriers (the empty asm statements keep each group
+  // of ops next to its MFMA; without them instruction selection moves the
+  // whole epilogue behind the last MFMA).
+  auto step = [&](const T (&bq)[4], T (&nxt)[4], bool load_next, int nbuf, int nblk, f32x4 (&acc)[4],
+                  const f32x4 (&prev)[4], const Unit* u) -> float {
+    const unsigned char* kn = reinterpret_cast<const unsigned char*>(nbuf ? ktile1 : ktile0) + nblk * kBlockBytes;
+    const f32x4 zero = {};
+    float sum = 0.f;
+    Slice z;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j + 2 < 8) bq[(j + 2) % 3] = frag(j + 2);
-      const T b = bq[j % 3];
-      acc[0] = M::run(A[0][j], b, j == 0 ? zero : acc[0]);
-      s0 = __builtin_fmaf(wr[0][2 * j], relu(prev[0][2 * j]), s0);
-      s1 = __builtin_fmaf(wr[1][2 * j], relu(prev[1][2 * j]), s1);
-      asm volatile("" : "+v"(s0), "+v"(s1));
-      __builtin_amdgcn_sched_barrier(0);
-      acc[1] = M::run(A[1][j], b, j == 0 ? zero : acc[1]);
-      s2 = __builtin_fmaf(wr[0][2 * j + 1], relu(prev[0][2 * j + 1]), s2);
-      s3 = __builtin_fmaf(wr[1][2 * j + 1], relu(prev[1][2 * j + 1]), s3);
-      asm volatile("" : "+v"(s2), "+v"(s3));
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int i = 4 * j + rb;
+        acc[rb] = M::run(A[rb][j], bq[j], j == 0 ? zero : acc[rb]);
+        sum = __builtin_fmaf(wr[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
+        asm volatile("" : "+v"(sum));
+        if (load_next && j == 0) nxt[rb] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kn + foff[rb]));
+        if (u) insert_slice(*u, i, z);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    return (s0 + s1) + (s2 + s3);
-  };
-  // 64 scores (two halves) into the top-k.  Most keys cannot enter once the
-  // buffer has been cut (v < score of tau): one f32 compare and a ballot
-  // dismiss them before any 64-bit key is formed.
-  auto insert_unit = [&](int s0, float p0, float p1, uint16_t mb, bool live) {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
-    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    const int s = s0 + lane;
-    const float v = (tot + f16_bits_to_f32(mb)) + 0.0f;
-    const bool vis = live && s >= wlo && s < whi && v != -__builtin_inff() && v >= st.tau_v;
-    if (ballot(vis) == 0ull) return;
-    wave_topk_insert(st, make_key(v, (uint32_t)s), vis);
+    return sum;
   };
 
   const int ntile = c1 - c0;
@@ -243,30 +357,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  f32x16 accA[2], accB[2];
+  f32x4 accA[4], accB[4];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) { accB[0][e] = 0.f; accB[1][e] = 0.f; }
-  float part0 = 0.f, part1 = 0.f, part2 = 0.f;
-  uint16_t mprev1 = 0;
-  // Pipeline over the four 32-key halves of each tile: step h issues the
-  // MFMAs of half h and finishes the epilogue of the half before it; every
-  // second step hands 64 finished scores to the top-k.
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { accA[rb][e] = 0.f; accB[rb][e] = 0.f; }
+  T bq0[4], bq1[4];
+  Unit u0, u1;  // keys 0-63 and 64-127 of a tile
+  u1.p[0] = u1.p[1] = u1.p[2] = 0.f;
+  u1.mb = 0;
+  // Pipeline over the eight 16-key blocks of each tile: step b issues the
+  // MFMAs of block b and finishes the head reduction of block b - 1.  The 64
+  // scores of blocks 0-3 are handed to the top-k during the step of block 5,
+  // those of blocks 4-7 during the step of block 1 of the next tile.
   auto tile_body = [&](int it, int buf) {
     const int tile = c0 + it;
+    frags(buf, 0, bq0);
     const uint16_t mc0 = mn0, mc1 = mn1;
-    if (it + 1 < ntile) {
+    const bool more = it + 1 < ntile;
+    if (more) {
       mn0 = mload((tile + 1) * TN);
       mn1 = mload((tile + 1) * TN + 64);
       gload(tile + 1, buf ^ 1);
     }
-    const float part3 = step(buf, 0, accA, accB);
-    insert_unit((tile - 1) * TN + 64, part2, part3, mprev1, it > 0);
-    part0 = step(buf, 1, accB, accA);
-    part1 = step(buf, 2, accA, accB);
-    insert_unit(tile * TN, part0, part1, mc0, true);
-    part2 = step(buf, 3, accB, accA);
-    mprev1 = mc1;
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's part of the next tile has landed in LDS
+    u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr);
+    u1.s0 = (tile - 1) * TN + 64;
+    u1.live = it > 0;
+    room();
+    u0.p[0] = step(bq1, bq0, true, buf, 2, accB, accA, &u1);
+    u0.p[1] = step(bq0, bq1, true, buf, 3, accA, accB, nullptr);
+    u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr);
+    u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr);
+    u0.s0 = tile * TN;
+    u0.mb = mc0;
+    u0.live = true;
+    room();
+    u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0);
+    u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr);
+    u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr);
+    u1.mb = mc1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed in LDS
     __syncthreads();
   };
   for (int it = 0; it < ntile; it += 2) {
@@ -274,7 +404,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     if (it + 1 >= ntile) break;
     tile_body(it + 1, 1);
   }
-  if (ntile > 0) insert_unit((c1 - 1) * TN + 64, part2, epilogue(accB), mprev1, true);
+  if (ntile > 0) {
+    u1.p[3] = epilogue(accB);
+    u1.s0 = (c1 - 1) * TN + 64;
+    u1.live = true;
+    room();
+    Slice z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) insert_slice(u1, i, z);
+  }
 
   if (has_q) {
     wave_topk_finish(st);
@@ -285,19 +423,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   }
 }
 
-template <int NW, int DT>
+template <int NW, int DT, bool MK>
 hipError_t launch_one(const KArgs& a, hipStream_t st) {
   const size_t lds = prefill_lds_bytes(NW, a.cap);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NW, DT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NW, DT, MK>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 2 * kTileBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t nqb = (a.n_tok + NW - 1) / NW;
   dim3 grid((unsigned)(nqb * a.P));
-  hipLaunchKernelGGL((prefill_kernel<NW, DT>), grid, dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((prefill_kernel<NW, DT, MK>), grid, dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
@@ -309,8 +447,13 @@ size_t prefill_lds_bytes(int nw, int cap) {
 }
 
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {
-  if (a.dtype == 1) return nw == 8 ? launch_one<8, 1>(a, st) : launch_one<4, 1>(a, st);
-  return nw == 8 ? launch_one<8, 2>(a, st) : launch_one<4, 2>(a, st);
+  const bool mk = a.mask != nullptr;
+  if (a.dtype == 1) {
+    if (nw == 8) return mk ? launch_one<8, 1, true>(a, st) : launch_one<8, 1, false>(a, st);
+    return mk ? launch_one<4, 1, true>(a, st) : launch_one<4, 1, false>(a, st);
+  }
+  if (nw == 8) return mk ? launch_one<8, 2, true>(a, st) : launch_one<8, 2, false>(a, st);
+  return mk ? launch_one<4, 2, true>(a, st) : launch_one<4, 2, false>(a, st);
 }
 
 }  // namespace lid
