@@ -96,6 +96,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   uint32_t* hist = reinterpret_cast<uint32_t*>(cand + (size_t)NW * a.cap);
   int64_t* rlo = reinterpret_cast<int64_t*>(hist + NW * 256);
   int64_t* rhi = rlo + NW;
+  uint32_t* cflag = reinterpret_cast<uint32_t*>(rhi + NW);  // [2][NW] compaction requests
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
@@ -247,7 +248,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // lane mask built on the scalar unit; the rest pass on v >= tau_v.  If any
   // lane passes, all 64 lanes store: passing keys at count + (rank among the
   // passing lanes), the others at count + n + lane, past the new count, where
-  // they are dead (the buffer always has 128 free slots here: see room()).
+  // they are dead (the buffer always has 128 free slots here: see
+  // flag_need()).
   // Adding the f16 mask to a sum that is never -0 cannot give -0 either, so
   // v needs no further canonicalisation.
   struct Unit {
@@ -302,19 +304,39 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
         const uint32_t n = (uint32_t)__popcll(m);
         const uint32_t c = (uint32_t)st.count;
         const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, c));
-        const uint32_t pos = pass ? rank : c + n + (uint32_t)lane;
+        const uint32_t pos = __float_as_uint(lane_select(m, __uint_as_float(rank), __uint_as_float(c + n + (uint32_t)lane)));
         const uint32_t b = __float_as_uint(z.v);
         const uint32_t khi = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);  // ord_f32
         const uint32_t klo = ~(uint32_t)(u.s0 + lane);
         st.buf[pos] = ((uint64_t)khi << 32) | klo;
-        st.count += (int)n;
+        st.count = (int)(c + n);
       }
     }
   };
   // Make room for one more unit: compaction to the k_top best when fewer than
   // 128 free slots remain (rare once the stream is long).
   auto room = [&]() {
+    st.count = __builtin_amdgcn_readfirstlane(st.count);  // keep it scalar (see uniform_u64)
     if (st.count > st.cap - 2 * kWave) wave_topk_reduce(st);
+  };
+  // Compactions are synchronised across the workgroup: a wave that could not
+  // take a whole further tile (two units) raises its flag before the tile
+  // barrier, and after the barrier every wave with more than k_top candidates
+  // compacts.  The waves meet at every tile barrier anyway, so one wave
+  // compacting alone would hold all of them; together they pay for it once.
+  // The flags are double buffered by tile parity: a wave can only rewrite a
+  // slot after the next barrier, which every reader of it has passed.
+  auto flag_need = [&](int it) {
+    if (lane == 0) cflag[(it & 1) * NW + wv] = st.count > st.cap - 3 * kWave ? 1u : 0u;
+  };
+  auto sync_compact = [&](int it) {
+    uint32_t any = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) any |= cflag[(it & 1) * NW + w2];
+    if (__builtin_amdgcn_readfirstlane(any)) {
+      st.count = __builtin_amdgcn_readfirstlane(st.count);
+      wave_topk_reduce(st);
+    }
   };
 
   // One pipeline step: the 16 MFMAs of the block whose B fragments are in bq
@@ -383,7 +405,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr);
     u1.s0 = (tile - 1) * TN + 64;
     u1.live = it > 0;
-    room();
     u0.p[0] = step(bq1, bq0, true, buf, 2, accB, accA, &u1);
     u0.p[1] = step(bq0, bq1, true, buf, 3, accA, accB, nullptr);
     u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr);
@@ -391,13 +412,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     u0.s0 = tile * TN;
     u0.mb = mc0;
     u0.live = true;
-    room();
     u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0);
     u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr);
     u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr);
     u1.mb = mc1;
+    flag_need(it);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed in LDS
     __syncthreads();
+    sync_compact(it);
   };
   for (int it = 0; it < ntile; it += 2) {
     tile_body(it, 0);
@@ -443,7 +465,7 @@ hipError_t launch_one(const KArgs& a, hipStream_t st) {
 
 // dynamic part only; the two key tiles (2 x 32 KiB) are static LDS
 size_t prefill_lds_bytes(int nw, int cap) {
-  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 8;
+  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 8 + 2 * (size_t)nw * 4;
 }
 
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {

@@ -67,7 +67,7 @@ int make_plan(const lid_shape* s, Plan* pl) {
   const bool mfma_ok = (s->qk_dtype == LID_F16 || s->qk_dtype == LID_BF16) && s->n_head == kMfmaHeads &&
                        s->head_dim == kMfmaDim;
   memset(pl, 0, sizeof(*pl));
-  pl->cap = 2 * K + 128;
+  pl->cap = 2 * K + 192;
   int kind = s->plan;
   if (kind == LID_PLAN_AUTO) {
     if (!mfma_ok) kind = LID_PLAN_GENERIC;

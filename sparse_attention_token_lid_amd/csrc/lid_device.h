@@ -243,12 +243,22 @@ __device__ __forceinline__ void wave_topk_init(WaveTopK& st, uint64_t* buf, uint
   st.tau_v = -__builtin_inff();
 }
 
+// The results are wave-uniform; readfirstlane says so to the compiler, which
+// otherwise keeps the count in a vector register (its loops over the buffer
+// have per-lane trip counts) and turns every later test of it into
+// exec-masked code.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
   if (st.count > st.K) {
-    uint64_t kap = wave_kth_largest(st.buf, st.count, st.K, st.hist);
-    st.count = wave_compact(st.buf, st.count, kap);
+    const uint64_t kap = uniform_u64(wave_kth_largest(st.buf, st.count, st.K, st.hist));
+    st.count = __builtin_amdgcn_readfirstlane(wave_compact(st.buf, st.count, kap));
     st.tau = kap;
-    st.tau_v = key_score(kap);
+    st.tau_v = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(key_score(kap))));
   }
 }
 
