@@ -42,6 +42,10 @@
  *    LID_ERR_HIP (a launch failed; outputs undefined).  There is no fallback
  *    to a path that would need an n_tok x n_kv buffer.
  *  - Calls that share one workspace must not overlap in time.
+ *  - The workspace must be zero-filled before its first use (the decode plan
+ *    keeps one 32-bit completion counter per query at its start); every call
+ *    that completes leaves those counters at zero again, so a workspace is
+ *    zeroed once and then reused freely, also from a captured HIP graph.
  */
 #ifndef LID_H
 #define LID_H
@@ -101,7 +105,8 @@ size_t lid_topk_workspace_size(const lid_shape* shape);
  *                               is an empty range
  *   idx       [n_tok, k_top]    int32 output
  *   score     [n_tok, k_top]    f32 output (the v of each returned key), or NULL
- *   workspace device scratch of >= lid_topk_workspace_size(shape) bytes
+ *   workspace device scratch of >= lid_topk_workspace_size(shape) bytes,
+ *             8-byte aligned, zero-filled before its first use (see above)
  *   stream    hipStream_t
  * Inputs must be finite (q, k, w); a NaN or +inf score is not detected. */
 int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* w,

@@ -141,7 +141,9 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
         score = torch.empty((n_tok, k_top), dtype=torch.float32, device=dev)
     ws_bytes = workspace_size(shape)
     if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        # zero-filled: the decode plan keeps per-query counters at its start,
+        # which must be zero before the first call (every call leaves them so)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream

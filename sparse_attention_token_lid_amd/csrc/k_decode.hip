@@ -1,5 +1,5 @@
 // k_decode.hip -- the few-query (decode) shape: one or a few query tokens
-// against a long key range, H = 64 heads, D = 128.
+// against a long key range, H = 64 heads, D = 128, in one kernel launch.
 //
 // Scoring is the same fused chain as the prefill kernel (per-head q.k, ReLU,
 // head weight, head sum, f16 mask; ggml-org llama.cpp issue 25468, "Root
@@ -9,13 +9,23 @@
 // loads are fully coalesced (64 lanes x 16 B = 1 KiB of consecutive bytes per
 // instruction), land in registers while the previous block is scored, and go
 // through a private LDS slot (XOR-swizzled) that turns them into the MFMA
-// B-operand layout.  The score of every key the workgroup sees goes to LDS as a
-// 64-bit selection key; the workgroup then selects its k_top best (radix
-// select + bitonic sort) and writes them as a sorted candidate list, which the
-// merge kernel reduces across splits.  Memory per split is bounded by the
-// LDS array, never by n_kv.
+// B-operand layout.
+//
+// The per-query top-k is finished by whichever workgroup of the query ends
+// last (a device-scope counter in the workspace, incremented with a wrapping
+// atomicInc, so it is back at zero after every launch).  Two forms:
+//  * raw (the query's range fits kRawMax positions): every workgroup writes
+//    its 32-bit ordered scores to the workspace and the last one selects the
+//    k_top best of all of them from registers: a lower bound of the k_top-th
+//    score (from per-thread maxima; 11-bit radix digit passes with
+//    per-wavefront LDS histograms when that bound is too loose) cuts them to
+//    a few thousand candidates, which are selected exactly and sorted in LDS;
+//  * lists: every workgroup selects the k_top best of its split (radix select
+//    + bitonic sort in LDS) and writes them as a sorted list; the last one
+//    merges the P lists (lid_merge.h).
 #include "lid_device.h"
 #include "lid_kernels.h"
+#include "lid_merge.h"
 
 namespace lid {
 namespace {
@@ -42,24 +52,398 @@ template <> struct Mfma<2> {
 constexpr int H = kMfmaHeads;
 constexpr int D = kMfmaDim;
 constexpr int NW = 8;     // wavefronts per workgroup
+constexpr int BS = NW * kWave;
 constexpr int KB = 32;    // keys per MFMA column block
 constexpr int kBlockBytes = KB * D * 2;          // 8 KiB per wavefront slot
 constexpr int kStageBytes = NW * kBlockBytes;    // 64 KiB
+static_assert(BS == kMergeThreads, "the last workgroup runs the merge");
+static_assert(kRawMax == BS * 64, "raw selection holds 64 positions per thread");
+
+constexpr int kRows = kRawMax / BS;   // positions per thread in the raw selection
+constexpr int kDigitBits = 11;        // radix digit of the raw selection
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kCandMax = 4096;        // candidates gathered into LDS for the exact select
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * D + ((ch ^ (row & 15)) << 3); }
 
-template <int DT>
-__global__ __launch_bounds__(NW * 64, 1) void decode_kernel(KArgs a, int keys_per_wg) {
+// ----------------------------------------------------------------- raw select
+// Block-wide reductions over one value per thread.
+__device__ inline uint32_t block_sum_u32(uint32_t x, uint32_t* red) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  x = wave_sum_u32(x);
+  if (lane == 0) red[wv] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) s += red[w2];
+  __syncthreads();
+  return s;
+}
+__device__ inline uint32_t block_and_u32(uint32_t x, uint32_t* red) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  x = wave_and_u32(x);
+  if (lane == 0) red[wv] = x;
+  __syncthreads();
+  uint32_t s = ~0u;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) s &= red[w2];
+  __syncthreads();
+  return s;
+}
+__device__ inline uint32_t block_or_u32(uint32_t x, uint32_t* red) {
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  x = wave_or_u32(x);
+  if (lane == 0) red[wv] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) s |= red[w2];
+  __syncthreads();
+  return s;
+}
+
+// Position of slot r of this thread in the raw row: 16-byte loads, thread
+// tid reading positions 2048 i + 4 tid + e for slot r = 4 i + e.
+__device__ __forceinline__ int raw_pos(int r, int tid) { return (r >> 2) * (4 * BS) + 4 * tid + (r & 3); }
+
+// Radix select over values held in registers, R per thread (0 = absent):
+// returns b with at least K present values >= b and b <= the K-th largest
+// present value (exactly the K-th largest when the values are unique), or 1
+// when fewer than K values are present.  8-bit digits from the highest bit in
+// which the values differ; per-wavefront LDS histograms (hw: 2 x NW x 256,
+// alternating between passes so each is cleared one pass ahead).
+template <typename KT, int R>
+__device__ __forceinline__ KT block_kth_largest_reg(const KT (&x)[R], uint32_t K, uint32_t* hw, BlockShared* sh,
+                                                    uint32_t* red) {
+  constexpr int BITS = 8 * (int)sizeof(KT);
+  const int tid = threadIdx.x, wv = tid / kWave;
+  KT an = ~(KT)0, on = 0;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    an &= x[i] ? x[i] : ~(KT)0;
+    on |= x[i];
+    c += x[i] ? 1u : 0u;
+  }
+  KT* rk = reinterpret_cast<KT*>(red);  // [2 NW] wave partials
+  if constexpr (BITS == 64) {
+    an = wave_and_u64(an);
+    on = wave_or_u64(on);
+  } else {
+    an = wave_and_u32(an);
+    on = wave_or_u32(on);
+  }
+  c = wave_sum_u32(c);
+  for (int i = tid; i < NW * 256; i += BS) hw[i] = 0u;  // first pass's histograms
+  if ((tid & (kWave - 1)) == 0) {
+    rk[wv] = an;
+    rk[NW + wv] = on;
+    red[4 * NW + wv] = c;
+  }
+  __syncthreads();
+  an = ~(KT)0;
+  on = 0;
+  c = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; ++w2) {
+    an &= rk[w2];
+    on |= rk[NW + w2];
+    c += red[4 * NW + w2];
+  }
+  __syncthreads();
+  if (c < K) return (KT)1;
+  if (an == on) return an;
+  const int top = BITS - 1 - (BITS == 64 ? __clzll((long long)(uint64_t)(an ^ on)) : __builtin_clz((uint32_t)(an ^ on)));
+  KT prefix = top == BITS - 1 ? (KT)0 : (an & ~(((KT)2 << top) - (KT)1));
+  uint32_t need = K;
+  int hi_bit = top;  // undecided bits: [hi_bit .. 0]
+  for (int pass = 0;; ++pass) {
+    const int nb = hi_bit + 1 < 8 ? hi_bit + 1 : 8;
+    const int shft = hi_bit + 1 - nb;
+    const uint32_t dmask = (1u << nb) - 1u;
+    uint32_t* h = hw + (pass & 1) * NW * 256;
+    uint32_t* hn = hw + ((pass + 1) & 1) * NW * 256;
+    uint32_t* mine = h + wv * 256;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const bool in = x[i] != 0 && (hi_bit >= BITS - 1 || (x[i] >> (hi_bit + 1)) == (prefix >> (hi_bit + 1)));
+      if (in) atomicAdd(&mine[(uint32_t)(x[i] >> shft) & dmask], 1u);
+    }
+    for (int i = tid; i < NW * 256; i += BS) hn[i] = 0u;
+    __syncthreads();
+    const int d = (int)dmask - tid;  // digits in descending order over the threads
+    uint32_t cnt = 0;
+    if (d >= 0) {
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) cnt += h[w2 * 256 + d];
+    }
+    int tot;
+    const uint32_t excl = (uint32_t)block_excl_scan((int)cnt, &tot, *sh);
+    if (d >= 0 && excl < need && need <= excl + cnt) {
+      sh->pick_d = (uint32_t)d;
+      sh->pick_above = excl;
+      sh->pick_cnt = cnt;
+    }
+    __syncthreads();
+    const uint32_t pd = sh->pick_d, above = sh->pick_above, pc = sh->pick_cnt;
+    prefix |= (KT)pd << shft;
+    need -= above;
+    if (pc == need || shft == 0) return prefix;  // lower bits zero: the bucket and above
+    hi_bit = shft - 1;
+  }
+}
+
+// Exact selection among m <= kCandMax candidate keys cand[0..m) (unique,
+// nonzero): the k_top best, sorted descending and padded with empty keys to
+// next_pow2(k_top), into sel.  The keys go to registers (kCandMax / BS per
+// thread) for block_kth_largest_reg; the keys >= the k_top-th are then
+// compacted with one block scan and sorted.
+__device__ __forceinline__ void select_candidates(const uint64_t* cand, int m, int K, uint64_t* sel, uint64_t* tmp,
+                                                  uint32_t* hw, BlockShared* sh, uint32_t* red) {
+  constexpr int R = kCandMax / BS;
+  const int tid = threadIdx.x;
+  uint64_t k[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int j = i * BS + tid;
+    k[i] = j < m ? cand[j] : 0ull;
+  }
+  const uint64_t thr = m > K ? block_kth_largest_reg<uint64_t, R>(k, (uint32_t)K, hw, sh, red) : 1ull;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) c += (k[i] != 0ull && k[i] >= thr) ? 1u : 0u;
+  int total;
+  int pos = block_excl_scan((int)c, &total, *sh);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (k[i] != 0ull && k[i] >= thr) sel[pos++] = k[i];
+  const int n2 = next_pow2(K);
+  for (int i = total + tid; i < n2; i += BS) sel[i] = 0ull;
+  __syncthreads();
+  block_sort_desc(sel, n2, tmp);
+}
+
+// The k_top best of the query's n ordered scores a.raw[row t][0..n) (0 = no
+// key there; position p is key lo + p), sorted, written as the output row.
+// A lower bound of the k_top-th score cuts the n values down to at most
+// kCandMax candidates (v >= thr, which hold the k_top best), which are
+// selected exactly as 64-bit keys (score, index).  The bound comes from the
+// per-thread maxima; when it leaves too many candidates, 11-bit radix digit
+// passes over the score word with per-wavefront LDS histograms find one.  If
+// a single score value is shared by more than kCandMax positions at the
+// threshold, the tied positions are taken in index order instead.
+__device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int64_t lo, unsigned char* smem) {
+  const int tid = threadIdx.x, wv = tid / kWave;
+  const int K = a.K, n2 = next_pow2(K);
+  uint32_t* hw = reinterpret_cast<uint32_t*>(smem);                    // [NW][kBins]
+  uint64_t* cand = reinterpret_cast<uint64_t*>(hw + NW * kBins);        // [kCandMax]
+  uint64_t* sel = cand + kCandMax;                                      // [n2]
+  uint64_t* tmp = sel + n2;                                             // [2 BS]
+  BlockShared* sh = reinterpret_cast<BlockShared*>(tmp + 2 * BS);
+  uint32_t* red = reinterpret_cast<uint32_t*>(sh + 1);                  // [4 NW + 8]
+
+  // agent-coherent (sc1) 16-byte loads; positions >= n read as 0 (the buffer
+  // resource ends there)
+  const uint32_t* row = a.raw + (size_t)t * a.raw_ld;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(row), (short)0, n * 4, 0x00020000);
+  uint32_t v[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows / 4; ++i) {
+    const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (i * 4 * BS + 4 * tid) * 4, 0, 16));
+    v[4 * i] = x[0]; v[4 * i + 1] = x[1]; v[4 * i + 2] = x[2]; v[4 * i + 3] = x[3];
+  }
+  // Each phase below re-derives its per-slot conditions from v; making v
+  // opaque between phases keeps the compiler from carrying 64 lane masks
+  // (128 scalar registers) from one phase to the next.
+  auto opaque = [&]() {
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) asm volatile("" : "+v"(v[r]));
+  };
+  opaque();
+  uint32_t c = 0, m1 = 0u, m2 = 0u;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const uint32_t x = v[r];
+    c += x < 1u ? x : 1u;  // present (integer min: no lane mask)
+    m2 = x > m1 ? m1 : (x > m2 ? x : m2);
+    m1 = x > m1 ? x : m1;
+  }
+  const uint32_t present = block_sum_u32(c, red);
+
+  uint32_t thr = 1u;        // candidates: v >= thr
+  bool tie_path = false;    // the k_top-th score is shared by too many positions
+  bool have_thr = present <= (uint32_t)K;  // then every present value is a candidate
+  if (!have_thr) {
+    // Lower bound of the k_top-th score: the k_top-th largest of the
+    // per-thread top-2 values (k_top of them are >= it, and it is one of the
+    // values); it usually leaves a few hundred candidates.
+    const uint32_t top2[2] = {m1, m2};
+    const uint32_t lb = block_kth_largest_reg<uint32_t, 2>(top2, (uint32_t)K, hw, sh, red);
+    opaque();
+    uint32_t cc = 0;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) cc += v[r] >= lb ? 1u : 0u;
+    if (block_sum_u32(cc, red) <= (uint32_t)kCandMax) {
+      thr = lb;
+      have_thr = true;
+    }
+  }
+  if (!have_thr) {
+    opaque();
+    uint32_t an = ~0u, on = 0u;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      an &= v[r] ? v[r] : ~0u;
+      on |= v[r];
+    }
+    an = block_and_u32(an, red);
+    on = block_or_u32(on, red);
+    if (an == on) {
+      thr = an;
+      tie_path = present > (uint32_t)kCandMax;
+    } else {
+      // digits below the bits all present values share
+      int top = 31 - __builtin_clz(an ^ on);
+      uint32_t prefix = top == 31 ? 0u : (an & ~((2u << top) - 1u));
+      uint32_t need = (uint32_t)K;
+      uint32_t gt = 0;  // values above the current digit bucket
+      for (;;) {
+        const int nb = top + 1 < kDigitBits ? top + 1 : kDigitBits;
+        const int shft = top + 1 - nb;
+        const uint32_t dmask = (1u << nb) - 1u;
+        const int msh = top + 1;  // bits at and above msh are fixed (== prefix)
+        for (int i = tid; i < NW * kBins; i += BS) hw[i] = 0u;
+        __syncthreads();
+        opaque();
+        uint32_t* h = hw + wv * kBins;
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+          const bool in = v[r] != 0u && (msh >= 32 || (v[r] >> msh) == (prefix >> msh));
+          if (in) atomicAdd(&h[(v[r] >> shft) & dmask], 1u);
+        }
+        __syncthreads();
+        // bins in descending digit order: thread tid owns digits d0 - j, j < kPer
+        constexpr int kPer = kBins / BS;
+        const int d0 = (int)dmask - kPer * tid;
+        uint32_t cb[kPer];
+        uint32_t s4 = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int d = d0 - j;
+          uint32_t x = 0;
+          if (d >= 0) {
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) x += hw[w2 * kBins + d];
+          }
+          cb[j] = x;
+          s4 += x;
+        }
+        int tot;
+        const uint32_t excl = (uint32_t)block_excl_scan((int)s4, &tot, *sh);
+        if (excl < need && need <= excl + s4) {
+          uint32_t above = excl;
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            if (above + cb[j] >= need) {
+              sh->pick_d = (uint32_t)(d0 - j);
+              sh->pick_above = above;
+              sh->pick_cnt = cb[j];
+              break;
+            }
+            above += cb[j];
+          }
+        }
+        __syncthreads();
+        const uint32_t d = sh->pick_d, above = sh->pick_above, dcnt = sh->pick_cnt;
+        __syncthreads();
+        prefix |= d << shft;
+        need -= above;
+        gt += above;
+        if (gt + dcnt <= (uint32_t)kCandMax) {
+          thr = prefix;  // lower bits zero: every value of the bucket and above
+          break;
+        }
+        if (shft == 0) {  // one exact score value, too many positions
+          thr = prefix;
+          tie_path = true;
+          break;
+        }
+        top = shft - 1;
+      }
+    }
+  }
+
+  // gather the candidates as 64-bit keys (score word, ~index)
+  int m = 0;
+  opaque();
+  if (!tie_path) {
+    uint64_t bits = 0ull;  // slot r of this thread is a candidate
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) bits |= (uint64_t)((v[r] != 0u && v[r] >= thr) ? 1u : 0u) << r;
+    int total;
+    int pos = block_excl_scan(__popcll(bits), &total, *sh);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      if ((bits >> r) & 1ull) {
+        const uint32_t s = (uint32_t)(lo + raw_pos(r, tid));
+        cand[pos++] = ((uint64_t)v[r] << 32) | (uint64_t)(~s);
+      }
+    }
+    m = total;
+  } else {
+    // everything above thr, then the first `need` positions (in index order)
+    // that score exactly thr: the cut position is found by bisection
+    auto gather = [&](auto pred, int base) -> int {
+      uint64_t bits = 0ull;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) bits |= (uint64_t)(pred(r) ? 1u : 0u) << r;
+      int total;
+      int pos = base + block_excl_scan(__popcll(bits), &total, *sh);
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        if ((bits >> r) & 1ull) {
+          const uint32_t s = (uint32_t)(lo + raw_pos(r, tid));
+          cand[pos++] = ((uint64_t)v[r] << 32) | (uint64_t)(~s);
+        }
+      }
+      return base + total;
+    };
+    const int above = gather([&](int r) { return v[r] > thr; }, 0);
+    const uint32_t need = (uint32_t)(K - above);
+    int x0 = 0, x1 = n;  // smallest x with #{tied positions < x} >= need
+    while (x0 < x1) {
+      const int mid = (x0 + x1) / 2;
+      uint32_t cc = 0;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) cc += (v[r] == thr && raw_pos(r, tid) < mid) ? 1u : 0u;
+      if (block_sum_u32(cc, red) >= need) x1 = mid;
+      else x0 = mid + 1;
+    }
+    m = gather([&](int r) { return v[r] == thr && raw_pos(r, tid) < x0; }, above);
+  }
+  __syncthreads();
+  select_candidates(cand, m, K, sel, tmp, hw, sh, red);
+  for (int i = tid; i < K; i += BS) {
+    a.idx[t * K + i] = key_index(sel[i]);
+    if (a.score) a.score[t * K + i] = key_score(sel[i]);
+  }
+}
+
+// ------------------------------------------------------------------- kernel
+template <int DT, bool RAW>
+__global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg, int ch) {
   using M = Mfma<DT>;
   using T = typename M::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* stage_all = reinterpret_cast<uint16_t*>(smem);           // [NW][KB * D]
-  uint64_t* arr = reinterpret_cast<uint64_t*>(smem + kStageBytes);   // [keys_per_wg]
+  uint64_t* arr = reinterpret_cast<uint64_t*>(smem + kStageBytes);   // [keys_per_wg] (lists form)
   uint64_t* sel = arr + keys_per_wg;                                 // [next_pow2(K)]
-  uint64_t* tmp = sel + next_pow2(a.K);                              // [2 * NW * 64]
-  BlockShared* sh = reinterpret_cast<BlockShared*>(tmp + 2 * NW * 64);
+  uint64_t* tmp = sel + next_pow2(a.K);                              // [2 * BS]
+  BlockShared* sh = reinterpret_cast<BlockShared*>(tmp + 2 * BS);
+  uint32_t* s_last = reinterpret_cast<uint32_t*>(sh + 1);
 
-  const int wv = threadIdx.x / kWave;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 5, m = lane & 31;
   const int P = a.P;
@@ -99,6 +483,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_kernel(KArgs a, int keys_pe
   const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
   const int64_t last_row = hi - 1;
   uint16_t* stage = stage_all + wv * (KB * D);
+  uint32_t* raw = RAW ? a.raw + (size_t)t * a.raw_ld : nullptr;
   auto load_blk = [&](int64_t b, u32x4 (&f)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -137,7 +522,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_kernel(KArgs a, int keys_pe
     const float v = (tot + f16_bits_to_f32(mbits)) + 0.0f;
     if (g == 0) {
       const bool valid = s < hi && v != -__builtin_inff();
-      arr[(b - b0) * KB + m] = valid ? make_key(v, (uint32_t)s) : 0ull;
+      if (RAW) __hip_atomic_store(&raw[b * KB + m], valid ? ord_f32(v) : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else arr[(b - b0) * KB + m] = valid ? make_key(v, (uint32_t)s) : 0ull;
     }
   };
 
@@ -160,43 +546,70 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_kernel(KArgs a, int keys_pe
   }
   __syncthreads();
 
-  block_select_sorted(arr, nkeys, a.K, sel, tmp, *sh);
-
-  if (P == 1) {
-    for (int i = threadIdx.x; i < a.K; i += blockDim.x) {
-      a.idx[t * a.K + i] = key_index(sel[i]);
-      if (a.score) a.score[t * a.K + i] = key_score(sel[i]);
+  if (!RAW) {
+    block_select_sorted(arr, nkeys, a.K, sel, tmp, *sh);
+    if (P == 1) {  // the only split: its list is the answer
+      for (int i = threadIdx.x; i < a.K; i += BS) {
+        a.idx[t * a.K + i] = key_index(sel[i]);
+        if (a.score) a.score[t * a.K + i] = key_score(sel[i]);
+      }
+      return;
     }
-  } else {
     uint64_t* out = a.lists + ((size_t)t * P + p) * a.K;
-    for (int i = threadIdx.x; i < a.K; i += blockDim.x) out[i] = sel[i];
+    for (int i = threadIdx.x; i < a.K; i += BS)
+      __hip_atomic_store(&out[i], sel[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+
+  // Publish this split's part, then let the last workgroup of the query
+  // finish.  The parts are written and read with agent-scope atomic stores
+  // and loads (coherent across the XCDs' separate L2 caches without writing
+  // back or invalidating them, which device-scope fences would do); every
+  // store has completed (vmcnt(0)) before the counter moves.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last[0] = __builtin_amdgcn_atomic_inc32(a.counters + t, (unsigned)(P - 1), __ATOMIC_RELAXED, "agent") ==
+                        (unsigned)(P - 1) ? 1u : 0u;
+  __syncthreads();
+  if (!s_last[0]) return;
+  if (RAW)
+    select_raw(a, t, (int)(nblk * KB), lo, smem);
+  else
+    merge_lists(a, ch, t, smem);
 }
 
-template <int DT>
-hipError_t launch_one(const KArgs& a, int keys_per_wg, hipStream_t st) {
+template <int DT, bool RAW>
+hipError_t launch_one(const KArgs& a, int keys_per_wg, int ch, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DT, RAW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)(a.n_tok * a.P));
-  hipLaunchKernelGGL((decode_kernel<DT>), grid, dim3(NW * 64), decode_lds_bytes(keys_per_wg, a.K), st, a,
-                     keys_per_wg);
+  hipLaunchKernelGGL((decode_kernel<DT, RAW>), grid, dim3(BS), decode_lds_bytes(keys_per_wg, a.K, a.P, ch, RAW), st,
+                     a, keys_per_wg, ch);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t decode_lds_bytes(int keys_per_wg, int K) {
-  return (size_t)kStageBytes + (size_t)keys_per_wg * 8 + (size_t)next_pow2(K) * 8 + 2 * NW * 64 * 8 +
-         sizeof(BlockShared);
+size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw) {
+  const size_t scoring = (size_t)kStageBytes + (size_t)keys_per_wg * 8 + (size_t)next_pow2(K) * 8 + 2 * BS * 8 +
+                         sizeof(BlockShared) + 16;
+  size_t finish;
+  if (raw)
+    finish = (size_t)NW * kBins * 4 + (size_t)kCandMax * 8 + (size_t)next_pow2(K) * 8 + 2 * BS * 8 +
+             sizeof(BlockShared) + (4 * NW + 8) * 4;
+  else
+    finish = P > 1 ? merge_lds_need(P, K, ch) : 0;
+  return scoring > finish ? scoring : finish;
 }
 
-hipError_t launch_decode(const KArgs& a, int keys_per_wg, hipStream_t st) {
-  return a.dtype == 1 ? launch_one<1>(a, keys_per_wg, st) : launch_one<2>(a, keys_per_wg, st);
+hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, bool raw, hipStream_t st) {
+  if (a.dtype == 1) return raw ? launch_one<1, true>(a, keys_per_wg, ch, st) : launch_one<1, false>(a, keys_per_wg, ch, st);
+  return raw ? launch_one<2, true>(a, keys_per_wg, ch, st) : launch_one<2, false>(a, keys_per_wg, ch, st);
 }
 
 }  // namespace lid

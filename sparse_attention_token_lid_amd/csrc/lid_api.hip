@@ -27,7 +27,10 @@ struct Plan {
   int cap;          // per-wave candidate capacity
   int keys_per_wg;  // decode: LDS key slots per workgroup
   int ch;           // merge: entries per list per round
+  bool raw;         // decode: raw-score form (the last workgroup selects from all scores)
+  int64_t raw_ld;   // decode, raw form: scores per query row
   size_t ws;        // workspace bytes
+  size_t ws_data;   // decode: offset of lists / raw scores (after the counters)
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -109,9 +112,21 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (kp < 32) kp = 32;
     if (kp > kDecodeMaxKeys) return LID_ERR_UNSUPPORTED;
     pl->keys_per_wg = (int)kp;
-    if (decode_lds_bytes(pl->keys_per_wg, K) > kMaxLds) return LID_ERR_UNSUPPORTED;
+    const int64_t span = cdiv(s->n_kv, 32) * 32;  // longest visible range, in 32-key blocks
+    pl->raw = span <= kRawMax;
+    if (P > 1) pl->ch = merge_chunk(P, K);
+    if (decode_lds_bytes(pl->keys_per_wg, K, P, pl->ch, pl->raw) > kMaxLds) return LID_ERR_UNSUPPORTED;
+    // workspace: per-query counters (zero between launches), then the raw
+    // scores or the per-split lists
+    pl->ws_data = (size_t)cdiv(s->n_tok * 4, 256) * 256;
+    if (pl->raw) {
+      pl->raw_ld = cdiv(span, 64) * 64;
+      pl->ws = pl->ws_data + (size_t)s->n_tok * pl->raw_ld * sizeof(uint32_t);
+    } else {
+      pl->ws = pl->ws_data + (P > 1 ? (size_t)s->n_tok * P * K * sizeof(uint64_t) : 0);
+    }
   }
-  if (pl->P > 1) {
+  if (pl->P > 1 && kind != LID_PLAN_DECODE) {
     pl->ch = merge_chunk(pl->P, K);
     if (merge_lds_bytes(pl->P, K, pl->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
     pl->ws = (size_t)s->n_tok * pl->P * K * sizeof(uint64_t);
@@ -168,6 +183,13 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   a.idx = idx;
   a.score = score;
   a.lists = reinterpret_cast<uint64_t*>(workspace);
+  if (pl.kind == LID_PLAN_DECODE) {
+    a.counters = reinterpret_cast<uint32_t*>(workspace);
+    unsigned char* data = reinterpret_cast<unsigned char*>(workspace) + pl.ws_data;
+    a.lists = reinterpret_cast<uint64_t*>(data);
+    a.raw = reinterpret_cast<uint32_t*>(data);
+    a.raw_ld = pl.raw_ld;
+  }
   a.n_tok = s.n_tok;
   a.n_kv = s.n_kv;
   a.mask_ld = mask ? s.mask_ld : 0;
@@ -182,11 +204,11 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   hipError_t e;
   if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
   if (pl.kind == LID_PLAN_PREFILL) e = launch_prefill(a, pl.nw, st);
-  else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, st);
+  else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, pl.ch, pl.raw, st);
   else e = launch_generic(a, st);
   if (e != hipSuccess) return hip_fail(e);
   if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
-  if (pl.P > 1) {
+  if (pl.P > 1 && pl.kind != LID_PLAN_DECODE) {
     e = launch_merge(a, pl.ch, st);
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -119,6 +119,22 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
   x += xor_lane_u32<32>(x);
   return x;
 }
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, Op op) {
+  x = op(x, xor_lane_u32<1>(x));
+  x = op(x, xor_lane_u32<2>(x));
+  x = op(x, xor_lane_u32<4>(x));
+  x = op(x, xor_lane_u32<8>(x));
+  x = op(x, xor_lane_u32<16>(x));
+  x = op(x, xor_lane_u32<32>(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a & b; });
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t x) {
+  return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a | b; });
+}
 // Inclusive prefix sum over the 64 lanes with DPP row shifts and row
 // broadcasts (no LDS traffic): within each row of 16 lanes, then rows 0-1
 // into row 1 / rows 2-3 into row 3 (row_bcast:15), then rows 0-1 into 2-3.
@@ -507,7 +523,7 @@ __device__ inline uint32_t block_key_stats(const uint64_t* arr, int n, uint64_t*
 
 // Descending sort of buf[0..n2) for a power of two n2 <= 1024: the unrolled
 // register network when n2 <= blockDim.x, else the LDS network.
-__device__ inline void block_sort_desc(uint64_t* buf, int n2, uint64_t* tmp) {
+__device__ __forceinline__ void block_sort_desc(uint64_t* buf, int n2, uint64_t* tmp) {
   if (n2 > (int)blockDim.x) { block_sort_desc_lds(buf, n2); return; }
   switch (n2) {
     case 1: break;

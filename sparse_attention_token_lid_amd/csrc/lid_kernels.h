@@ -16,7 +16,9 @@ struct KArgs {
   int32_t* idx;             // [n_tok, K]
   float* score;             // [n_tok, K], or null
   uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1)
-  int64_t n_tok, n_kv, mask_ld;
+  uint32_t* raw;            // decode, raw form: [n_tok, raw_ld] ordered scores (0 = no key)
+  uint32_t* counters;       // decode: [n_tok] finished-workgroup counters (zero between launches)
+  int64_t n_tok, n_kv, mask_ld, raw_ld;
   int32_t H, D, K, P;
   int32_t cap;              // per-wave candidate buffer capacity (entries)
   int32_t dtype;            // 0 f32, 1 f16, 2 bf16
@@ -27,13 +29,14 @@ constexpr int kMfmaHeads = 64;
 constexpr int kMfmaDim = 128;
 constexpr int kPrefillTile = 128;      // keys per LDS tile
 constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
+constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);
 size_t prefill_lds_bytes(int nw, int cap);
 
-hipError_t launch_decode(const KArgs& a, int keys_per_wg, hipStream_t st);
-size_t decode_lds_bytes(int keys_per_wg, int K);
+hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, bool raw, hipStream_t st);
+size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw);
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st);
 size_t merge_lds_bytes(int P, int K, int ch);

@@ -59,11 +59,20 @@ def test_auto_plans_and_workspace(L, name, plan):
     assert got == plan
     ws = L.workspace_size(s)
     wl = li.WORKLOADS[name]
-    assert ws == (wl.n_tok * splits * wl.k_top * 8 if splits > 1 else 0)
+    lists = wl.n_tok * splits * wl.k_top * 8 if splits > 1 else 0
+    if plan == "decode":
+        # per-query counters (256-byte rounded), then either every 32-bit
+        # score of the query (ranges up to 32768 keys) or the split lists
+        counters = -(-wl.n_tok * 4 // 256) * 256
+        span = -(-wl.n_kv // 32) * 32
+        raw = wl.n_tok * (-(-span // 64) * 64) * 4
+        assert ws == counters + (raw if span <= 32768 else lists)
+    else:
+        assert ws == lists
     # O(n_tok * k_top * splits) with splits <= 256, whatever n_kv is
-    assert splits <= 256 and ws <= wl.n_tok * wl.k_top * 8 * 256
+    assert splits <= 256 and ws <= 256 * -(-wl.n_tok * 4 // 256) + wl.n_tok * wl.k_top * 8 * 256
     if wl.n_kv >= 131072:
-        assert ws <= wl.n_tok * wl.n_kv * 4 // 4   # well below even the f32 score matrix
+        assert ws <= wl.n_tok * wl.n_kv * 4 // 4 + 256   # well below even the f32 score matrix
 
 
 def call(L, shape, q=16, k=16, w=16, mask=None, rng=None, idx=16, score=None, ws=None, ws_bytes=0):

@@ -225,7 +225,7 @@ def test_no_score_matrix_allocated(lid, name):
     _, splits = lid.plan_of(shape)
     assert ws_bytes == wl.n_tok * splits * wl.k_top * 8 if splits > 1 else ws_bytes == 0
     assert ws_bytes < wl.n_tok * wl.n_kv * 4 / 8   # < 1/8 of even the f32 score matrix
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     idx = torch.empty((wl.n_tok, wl.k_top), dtype=torch.int32, device="cuda")
     sc = torch.empty((wl.n_tok, wl.k_top), dtype=torch.float32, device="cuda")
     lid.topk(qd, kd, wd, kv_range=rd, k_top=wl.k_top, idx=idx, score=sc, workspace=ws)  # warm up
