@@ -26,6 +26,7 @@
 #include "lid_device.h"
 #include "lid_kernels.h"
 #include "lid_merge.h"
+#include "lid_select.h"
 
 namespace lid {
 namespace {
@@ -56,7 +57,7 @@ constexpr int BS = NW * kWave;
 constexpr int KB = 32;    // keys per MFMA column block
 constexpr int kBlockBytes = KB * D * 2;          // 8 KiB per wavefront slot
 constexpr int kStageBytes = NW * kBlockBytes;    // 64 KiB
-static_assert(BS == kMergeThreads, "the last workgroup runs the merge");
+static_assert(BS == kMergeThreads && BS == kSelThreads, "the last workgroup runs the merge");
 static_assert(kRawMax == BS * 64, "raw selection holds 64 positions per thread");
 
 constexpr int kRows = kRawMax / BS;   // positions per thread in the raw selection
@@ -105,123 +106,6 @@ __device__ inline uint32_t block_or_u32(uint32_t x, uint32_t* red) {
 // Position of slot r of this thread in the raw row: 16-byte loads, thread
 // tid reading positions 2048 i + 4 tid + e for slot r = 4 i + e.
 __device__ __forceinline__ int raw_pos(int r, int tid) { return (r >> 2) * (4 * BS) + 4 * tid + (r & 3); }
-
-// Radix select over values held in registers, R per thread (0 = absent):
-// returns b with at least K present values >= b and b <= the K-th largest
-// present value (exactly the K-th largest when the values are unique), or 1
-// when fewer than K values are present.  8-bit digits from the highest bit in
-// which the values differ; per-wavefront LDS histograms (hw: 2 x NW x 256,
-// alternating between passes so each is cleared one pass ahead).
-template <typename KT, int R>
-__device__ __forceinline__ KT block_kth_largest_reg(const KT (&x)[R], uint32_t K, uint32_t* hw, BlockShared* sh,
-                                                    uint32_t* red) {
-  constexpr int BITS = 8 * (int)sizeof(KT);
-  const int tid = threadIdx.x, wv = tid / kWave;
-  KT an = ~(KT)0, on = 0;
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    an &= x[i] ? x[i] : ~(KT)0;
-    on |= x[i];
-    c += x[i] ? 1u : 0u;
-  }
-  KT* rk = reinterpret_cast<KT*>(red);  // [2 NW] wave partials
-  if constexpr (BITS == 64) {
-    an = wave_and_u64(an);
-    on = wave_or_u64(on);
-  } else {
-    an = wave_and_u32(an);
-    on = wave_or_u32(on);
-  }
-  c = wave_sum_u32(c);
-  for (int i = tid; i < NW * 256; i += BS) hw[i] = 0u;  // first pass's histograms
-  if ((tid & (kWave - 1)) == 0) {
-    rk[wv] = an;
-    rk[NW + wv] = on;
-    red[4 * NW + wv] = c;
-  }
-  __syncthreads();
-  an = ~(KT)0;
-  on = 0;
-  c = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < NW; ++w2) {
-    an &= rk[w2];
-    on |= rk[NW + w2];
-    c += red[4 * NW + w2];
-  }
-  __syncthreads();
-  if (c < K) return (KT)1;
-  if (an == on) return an;
-  const int top = BITS - 1 - (BITS == 64 ? __clzll((long long)(uint64_t)(an ^ on)) : __builtin_clz((uint32_t)(an ^ on)));
-  KT prefix = top == BITS - 1 ? (KT)0 : (an & ~(((KT)2 << top) - (KT)1));
-  uint32_t need = K;
-  int hi_bit = top;  // undecided bits: [hi_bit .. 0]
-  for (int pass = 0;; ++pass) {
-    const int nb = hi_bit + 1 < 8 ? hi_bit + 1 : 8;
-    const int shft = hi_bit + 1 - nb;
-    const uint32_t dmask = (1u << nb) - 1u;
-    uint32_t* h = hw + (pass & 1) * NW * 256;
-    uint32_t* hn = hw + ((pass + 1) & 1) * NW * 256;
-    uint32_t* mine = h + wv * 256;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const bool in = x[i] != 0 && (hi_bit >= BITS - 1 || (x[i] >> (hi_bit + 1)) == (prefix >> (hi_bit + 1)));
-      if (in) atomicAdd(&mine[(uint32_t)(x[i] >> shft) & dmask], 1u);
-    }
-    for (int i = tid; i < NW * 256; i += BS) hn[i] = 0u;
-    __syncthreads();
-    const int d = (int)dmask - tid;  // digits in descending order over the threads
-    uint32_t cnt = 0;
-    if (d >= 0) {
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) cnt += h[w2 * 256 + d];
-    }
-    int tot;
-    const uint32_t excl = (uint32_t)block_excl_scan((int)cnt, &tot, *sh);
-    if (d >= 0 && excl < need && need <= excl + cnt) {
-      sh->pick_d = (uint32_t)d;
-      sh->pick_above = excl;
-      sh->pick_cnt = cnt;
-    }
-    __syncthreads();
-    const uint32_t pd = sh->pick_d, above = sh->pick_above, pc = sh->pick_cnt;
-    prefix |= (KT)pd << shft;
-    need -= above;
-    if (pc == need || shft == 0) return prefix;  // lower bits zero: the bucket and above
-    hi_bit = shft - 1;
-  }
-}
-
-// Exact selection among m <= kCandMax candidate keys cand[0..m) (unique,
-// nonzero): the k_top best, sorted descending and padded with empty keys to
-// next_pow2(k_top), into sel.  The keys go to registers (kCandMax / BS per
-// thread) for block_kth_largest_reg; the keys >= the k_top-th are then
-// compacted with one block scan and sorted.
-__device__ __forceinline__ void select_candidates(const uint64_t* cand, int m, int K, uint64_t* sel, uint64_t* tmp,
-                                                  uint32_t* hw, BlockShared* sh, uint32_t* red) {
-  constexpr int R = kCandMax / BS;
-  const int tid = threadIdx.x;
-  uint64_t k[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int j = i * BS + tid;
-    k[i] = j < m ? cand[j] : 0ull;
-  }
-  const uint64_t thr = m > K ? block_kth_largest_reg<uint64_t, R>(k, (uint32_t)K, hw, sh, red) : 1ull;
-  uint32_t c = 0;
-#pragma unroll
-  for (int i = 0; i < R; ++i) c += (k[i] != 0ull && k[i] >= thr) ? 1u : 0u;
-  int total;
-  int pos = block_excl_scan((int)c, &total, *sh);
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-    if (k[i] != 0ull && k[i] >= thr) sel[pos++] = k[i];
-  const int n2 = next_pow2(K);
-  for (int i = total + tid; i < n2; i += BS) sel[i] = 0ull;
-  __syncthreads();
-  block_sort_desc(sel, n2, tmp);
-}
 
 // The k_top best of the query's n ordered scores a.raw[row t][0..n) (0 = no
 // key there; position p is key lo + p), sorted, written as the output row.
@@ -423,7 +307,7 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
     m = gather([&](int r) { return v[r] == thr && raw_pos(r, tid) < x0; }, above);
   }
   __syncthreads();
-  select_candidates(cand, m, K, sel, tmp, hw, sh, red);
+  block_select_sorted_reg<kCandMax / BS>(cand, m, K, sel, tmp, hw, sh, red);
   for (int i = tid; i < K; i += BS) {
     a.idx[t * K + i] = key_index(sel[i]);
     if (a.score) a.score[t * K + i] = key_score(sel[i]);
@@ -547,7 +431,9 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   __syncthreads();
 
   if (!RAW) {
-    block_select_sorted(arr, nkeys, a.K, sel, tmp, *sh);
+    // the stage buffers are free now: histograms and reduction slots
+    block_select_sorted_reg<kDecodeMaxKeys / BS>(arr, nkeys, a.K, sel, tmp, reinterpret_cast<uint32_t*>(smem), sh,
+                                                 reinterpret_cast<uint32_t*>(smem + kSelHistBytes));
     if (P == 1) {  // the only split: its list is the answer
       for (int i = threadIdx.x; i < a.K; i += BS) {
         a.idx[t * a.K + i] = key_index(sel[i]);

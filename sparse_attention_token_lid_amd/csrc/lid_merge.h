@@ -15,6 +15,7 @@
 #pragma once
 #include "lid_device.h"
 #include "lid_kernels.h"
+#include "lid_select.h"
 
 namespace lid {
 
@@ -24,10 +25,10 @@ constexpr int kMergeThreads = 512;
 __host__ __device__ inline size_t merge_lds_need(int P, int K, int ch) {
   const size_t capm = (size_t)K + (size_t)P * ch;
   return capm * 8 + (size_t)next_pow2(K) * 8 + 2 * kMergeThreads * 8 + (size_t)P * 8 + sizeof(BlockShared) +
-         2 * sizeof(int) + 2 * (size_t)P;
+         2 * sizeof(int) + 2 * (size_t)P + 16 + kSelHistBytes + kSelRedBytes;
 }
 
-__device__ inline void merge_lists(const KArgs& a, int ch, int64_t t, unsigned char* smem) {
+__device__ __forceinline__ void merge_lists(const KArgs& a, int ch, int64_t t, unsigned char* smem) {
   const int P = a.P, K = a.K;
   const int n2 = next_pow2(K);
   const int capm = K + P * ch;
@@ -41,10 +42,14 @@ __device__ inline void merge_lists(const KArgs& a, int ch, int64_t t, unsigned c
   int& s_active = counters[1];
   uint8_t* done = reinterpret_cast<uint8_t*>(counters + 2);    // [P]
   uint8_t* done_next = done + P;                               // [P]
+  uint32_t* hw = reinterpret_cast<uint32_t*>(                  // selection histograms, 16-byte aligned
+      (reinterpret_cast<uintptr_t>(done_next + P) + 15) & ~static_cast<uintptr_t>(15));
+  uint32_t* red = hw + kSelHistBytes / 4;
+  static_assert(18 * kMergeThreads >= 1024 + 8192, "capm <= K + P ch <= 1024 + 8192");
 
   const uint64_t* lists = a.lists + (size_t)t * P * K;
   for (int i = threadIdx.x; i < P; i += kMergeThreads) { done[i] = 0; done_next[i] = 0; }
-  if (threadIdx.x == 0) s_count = 0;
+  if (threadIdx.x == 0) { s_count = 0; sh->red_min = ~0ull; }
   __syncthreads();
 
   uint64_t tau = 0ull;
@@ -89,12 +94,20 @@ __device__ inline void merge_lists(const KArgs& a, int ch, int64_t t, unsigned c
     // keep the K best; their K-th key bounds the final threshold from below,
     // and every list whose last key read is below it is finished
     if (count > K && (r == 0 || count + P * ch > capm)) {
-      uint64_t ka, ko;
-      block_key_stats(cand, count, &ka, &ko, *sh);
-      const uint64_t kap = block_kth_largest(cand, count, K, ka, ko, *sh);
-      const int kept = block_compact(cand, count, kap, sel, *sh);
-      for (int i = threadIdx.x; i < kept; i += kMergeThreads) cand[i] = sel[i];
+      const int kept = block_select_compact_any(cand, count, K, sel, hw, sh, red);
+      // kept == K: their minimum is the K-th key
+      uint64_t mn = ~0ull;
+      for (int i = threadIdx.x; i < kept; i += kMergeThreads) {
+        cand[i] = sel[i];
+        mn = sel[i] < mn ? sel[i] : mn;
+      }
+      mn = wave_min_u64(mn);
+      if (lane_id() == 0) atomicMin((unsigned long long*)&sh->red_min, mn);
       if (threadIdx.x == 0) s_count = kept;
+      __syncthreads();
+      const uint64_t kap = sh->red_min;
+      __syncthreads();
+      if (threadIdx.x == 0) sh->red_min = ~0ull;
       tau = kap;
       for (int i = threadIdx.x; i < P; i += kMergeThreads)
         if (last[i] <= tau) done[i] = 1;
@@ -110,7 +123,7 @@ __device__ inline void merge_lists(const KArgs& a, int ch, int64_t t, unsigned c
     __syncthreads();
     block_sort_desc(sel, n2, tmp);
   } else {
-    block_select_sorted(cand, count, K, sel, tmp, *sh);
+    block_select_sorted_any(cand, count, K, sel, tmp, hw, sh, red);
   }
   for (int i = threadIdx.x; i < K; i += kMergeThreads) {
     a.idx[t * K + i] = key_index(sel[i]);

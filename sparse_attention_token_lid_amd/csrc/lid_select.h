@@ -1,0 +1,166 @@
+// lid_select.h -- block-wide exact selection with the keys held in
+// registers (used by the decode kernel and the merge; workgroups of kSelThreads
+// threads).  A radix select with 8-bit digits from the highest bit in which
+// the keys differ: the keys are counted into a shared LDS histogram and every
+// wavefront finds the digit that holds the K-th largest key from it; no LDS
+// array of keys is rescanned per pass and a pass costs one barrier.
+#pragma once
+#include "lid_device.h"
+
+namespace lid {
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+// LDS the helpers need besides their key arrays: histograms and a small
+// reduction area.
+constexpr size_t kSelHistBytes = 2 * kSelWaves * 256 * 4;
+constexpr size_t kSelRedBytes = (4 * kSelWaves + 8) * 4;
+
+// Radix select over values held in registers, R per thread (0 = absent):
+// returns b with at least K present values >= b and b <= the K-th largest
+// present value (exactly the K-th largest when the values are unique), or 1
+// when fewer than K values are present.  8-bit digits from the highest bit in
+// which the values differ; one shared 256-bin LDS histogram per pass (three
+// rotate, each cleared two passes ahead), and every wavefront finds the digit
+// from it itself, so a pass costs a single barrier.  hw is unused (kept for
+// the callers' layout).
+template <typename KT, int R>
+__device__ __forceinline__ KT block_kth_largest_reg(const KT (&xin)[R], uint32_t K, uint32_t* hw, BlockShared* sh,
+                                                    uint32_t* red) {
+  (void)hw;
+  (void)red;
+  constexpr int BITS = 8 * (int)sizeof(KT);
+  const int tid = threadIdx.x;
+  // a private copy, made opaque at every pass so that per-key conditions are
+  // recomputed (cheap) instead of being kept live as lane masks across passes
+  KT x[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) x[i] = xin[i];
+  KT an = ~(KT)0, on = 0;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    an &= x[i] ? x[i] : ~(KT)0;
+    on |= x[i];
+    c += x[i] ? 1u : 0u;
+  }
+  if constexpr (BITS == 64) {
+    an = wave_and_u64(an);
+    on = wave_or_u64(on);
+  } else {
+    an = wave_and_u32(an);
+    on = wave_or_u32(on);
+  }
+  c = wave_sum_u32(c);
+  if (tid == 0) { sh->red_and = ~0ull; sh->red_or = 0ull; sh->nz = 0u; }
+  for (int i = tid; i < 3 * 256; i += kSelThreads) (&sh->hist[0][0])[i] = 0u;
+  __syncthreads();
+  if ((tid & (kWave - 1)) == 0) {
+    atomicAnd((unsigned long long*)&sh->red_and, (unsigned long long)an);
+    atomicOr((unsigned long long*)&sh->red_or, (unsigned long long)on);
+    atomicAdd(&sh->nz, c);
+  }
+  __syncthreads();
+  an = (KT)sh->red_and;
+  on = (KT)sh->red_or;
+  c = sh->nz;
+  if (c < K) return (KT)1;
+  if (an == on) return an;
+  const int top = BITS - 1 - (BITS == 64 ? __clzll((long long)(uint64_t)(an ^ on)) : __builtin_clz((uint32_t)(an ^ on)));
+  KT prefix = top == BITS - 1 ? (KT)0 : (an & ~(((KT)2 << top) - (KT)1));
+  uint32_t need = K;
+  int hi_bit = top;  // undecided bits: [hi_bit .. 0]
+  for (int pass = 0;; ++pass) {
+    const int nb = hi_bit + 1 < 8 ? hi_bit + 1 : 8;
+    const int shft = hi_bit + 1 - nb;
+    const uint32_t dmask = (1u << nb) - 1u;
+    uint32_t* h = sh->hist[pass % 3];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if constexpr (sizeof(KT) == 8) {
+        uint32_t lo = (uint32_t)x[i], hi = (uint32_t)(x[i] >> 32);
+        asm volatile("" : "+v"(lo), "+v"(hi));
+        x[i] = ((KT)hi << 32) | lo;
+      } else {
+        asm volatile("" : "+v"(x[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const bool in = x[i] != 0 && (hi_bit >= BITS - 1 || (x[i] >> (hi_bit + 1)) == (prefix >> (hi_bit + 1)));
+      if (in) atomicAdd(&h[(uint32_t)(x[i] >> shft) & dmask], 1u);
+    }
+    __syncthreads();
+    // digits above dmask stay zero, so the 256-bin search sees the nb-bit digit
+    const DigitPick pk = pick_digit(h, need);
+    for (int i = tid; i < 256; i += kSelThreads) sh->hist[(pass + 2) % 3][i] = 0u;
+    prefix |= (KT)pk.d << shft;
+    need -= pk.above;
+    if (pk.cnt == need || shft == 0) return prefix;  // lower bits zero: the bucket and above
+    hi_bit = shft - 1;
+  }
+}
+
+// The K best of arr[0..n) (n <= R * kSelThreads; unique keys, 0 = empty), in
+// no particular order, into dst; returns how many (min(K, keys present)).
+template <int R>
+__device__ __forceinline__ int block_select_compact_reg(const uint64_t* arr, int n, int K, uint64_t* dst,
+                                                        uint32_t* hw, BlockShared* sh, uint32_t* red) {
+  const int tid = threadIdx.x;
+  uint64_t k[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int j = i * kSelThreads + tid;
+    k[i] = j < n ? arr[j] : 0ull;
+  }
+  const uint64_t thr = n > K ? block_kth_largest_reg<uint64_t, R>(k, (uint32_t)K, hw, sh, red) : 1ull;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {  // opaque: see block_kth_largest_reg
+    uint32_t lo = (uint32_t)k[i], hi = (uint32_t)(k[i] >> 32);
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    k[i] = ((uint64_t)hi << 32) | lo;
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i) c += (k[i] != 0ull && k[i] >= thr) ? 1u : 0u;
+  int total;
+  int pos = block_excl_scan((int)c, &total, *sh);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (k[i] != 0ull && k[i] >= thr) dst[pos++] = k[i];
+  __syncthreads();
+  return total;
+}
+
+// The K best of arr[0..n), sorted descending and padded with empty keys to
+// next_pow2(K), into sel (tmp: 2 kSelThreads entries for the sort).
+template <int R>
+__device__ __forceinline__ void block_select_sorted_reg(const uint64_t* arr, int n, int K, uint64_t* sel,
+                                                        uint64_t* tmp, uint32_t* hw, BlockShared* sh, uint32_t* red) {
+  const int m = block_select_compact_reg<R>(arr, n, K, sel, hw, sh, red);
+  const int n2 = next_pow2(K);
+  for (int i = m + (int)threadIdx.x; i < n2; i += kSelThreads) sel[i] = 0ull;
+  __syncthreads();
+  block_sort_desc(sel, n2, tmp);
+}
+
+// The same with the register count chosen from n at run time (n is
+// block-uniform), so a small set is not scanned through empty slots.
+__device__ __forceinline__ int block_select_compact_any(const uint64_t* arr, int n, int K, uint64_t* dst, uint32_t* hw,
+                                                        BlockShared* sh, uint32_t* red) {
+  if (n <= 2 * kSelThreads) return block_select_compact_reg<2>(arr, n, K, dst, hw, sh, red);
+  if (n <= 4 * kSelThreads) return block_select_compact_reg<4>(arr, n, K, dst, hw, sh, red);
+  if (n <= 8 * kSelThreads) return block_select_compact_reg<8>(arr, n, K, dst, hw, sh, red);
+  if (n <= 16 * kSelThreads) return block_select_compact_reg<16>(arr, n, K, dst, hw, sh, red);
+  return block_select_compact_reg<18>(arr, n, K, dst, hw, sh, red);  // n <= 18 kSelThreads (callers check)
+}
+__device__ __forceinline__ void block_select_sorted_any(const uint64_t* arr, int n, int K, uint64_t* sel,
+                                                        uint64_t* tmp, uint32_t* hw, BlockShared* sh, uint32_t* red) {
+  const int m = block_select_compact_any(arr, n, K, sel, hw, sh, red);
+  const int n2 = next_pow2(K);
+  for (int i = m + (int)threadIdx.x; i < n2; i += kSelThreads) sel[i] = 0ull;
+  __syncthreads();
+  block_sort_desc(sel, n2, tmp);
+}
+
+}  // namespace lid
