@@ -432,8 +432,12 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
 
   if (!RAW) {
     // the stage buffers are free now: histograms and reduction slots
-    block_select_sorted_reg<kDecodeMaxKeys / BS>(arr, nkeys, a.K, sel, tmp, reinterpret_cast<uint32_t*>(smem), sh,
-                                                 reinterpret_cast<uint32_t*>(smem + kSelHistBytes));
+    uint32_t* shw = reinterpret_cast<uint32_t*>(smem);
+    uint32_t* sred = reinterpret_cast<uint32_t*>(smem + kSelHistBytes);
+    if (nkeys <= 8 * BS)
+      block_select_sorted_reg<8>(arr, nkeys, a.K, sel, tmp, shw, sh, sred);
+    else
+      block_select_sorted_reg<kDecodeMaxKeys / BS>(arr, nkeys, a.K, sel, tmp, shw, sh, sred);
     if (P == 1) {  // the only split: its list is the answer
       for (int i = threadIdx.x; i < a.K; i += BS) {
         a.idx[t * a.K + i] = key_index(sel[i]);
