@@ -317,11 +317,72 @@ __host__ __device__ constexpr int next_pow2(int x) {
   return p;
 }
 
+// Descending bitonic sort of 64 E keys held in registers by one wavefront,
+// lane L holding elements E L .. E L + E - 1 in x[0..E).  A compare-exchange
+// at element distance j < E stays inside one lane's registers; one at
+// distance j >= E pairs lanes L and L ^ (j / E), exchanged with DPP or a
+// permlane swap.  No LDS and no barrier; E independent chains per stage.
+template <int E, int K, int J>
+__device__ __forceinline__ void wave_bitonic_stage_reg(uint64_t (&x)[E], int lane) {
+  if constexpr (J < E) {
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+      if (s & J) continue;
+      bool desc;  // the run holding element E lane + s is sorted descending
+      if constexpr (K < E) desc = (s & K) == 0;
+      else desc = (lane & (K / E)) == 0;
+      const uint64_t a = x[s], b = x[s | J];
+      const bool sw = desc ? (a < b) : (a > b);
+      x[s] = sw ? b : a;
+      x[s | J] = sw ? a : b;
+    }
+  } else {
+    constexpr int D = J / E;
+    const bool low = (lane & D) == 0;  // this lane holds the lower element of each pair
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+      const uint64_t y = xor_lane_u64<D>(x[s]);
+      bool desc;
+      if constexpr (K < E) desc = (s & K) == 0;
+      else desc = (lane & (K / E)) == 0;
+      const bool take_max = desc == low;
+      x[s] = (take_max == (x[s] > y)) ? x[s] : y;
+    }
+  }
+}
+template <int E, int K, int J>
+__device__ __forceinline__ void wave_bitonic_merge_reg(uint64_t (&x)[E], int lane) {
+  wave_bitonic_stage_reg<E, K, J>(x, lane);
+  if constexpr (J > 1) wave_bitonic_merge_reg<E, K, J / 2>(x, lane);
+}
+template <int E, int K = 2>
+__device__ __forceinline__ void wave_sort_reg(uint64_t (&x)[E], int lane) {
+  wave_bitonic_merge_reg<E, K, K / 2>(x, lane);
+  if constexpr (K < kWave * E) wave_sort_reg<E, K * 2>(x, lane);
+}
+
+// buf[0..64 E) sorted descending in place through registers (entries at or
+// past n are taken as empty keys).
+template <int E>
+__device__ __forceinline__ void wave_sort_desc_reg(uint64_t* buf, int n) {
+  const int lane = lane_id();
+  uint64_t x[E];
+#pragma unroll
+  for (int s = 0; s < E; ++s) x[s] = (E * lane + s < n) ? buf[E * lane + s] : 0ull;
+  wave_sort_reg<E>(x, lane);
+#pragma unroll
+  for (int s = 0; s < E; ++s) buf[E * lane + s] = x[s];
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Cut to the K best, sort descending and pad with empty keys to K entries.
 // Needs cap >= next_pow2(K).  Result in buf[0..K).
 __device__ inline void wave_topk_finish(WaveTopK& st) {
   wave_topk_reduce(st);
   const int n2 = next_pow2(st.K);
+  if (n2 == 256) { wave_sort_desc_reg<4>(st.buf, st.count); return; }
+  if (n2 == 512) { wave_sort_desc_reg<8>(st.buf, st.count); return; }
+  if (n2 == 1024) { wave_sort_desc_reg<16>(st.buf, st.count); return; }
   for (int i = st.count + lane_id(); i < n2; i += kWave) st.buf[i] = 0ull;
   __builtin_amdgcn_wave_barrier();
   wave_sort_desc(st.buf, n2);
