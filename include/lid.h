@@ -43,7 +43,9 @@
  *    to a path that would need an n_tok x n_kv buffer.
  *  - Calls that share one workspace must not overlap in time.
  *  - The workspace must be zero-filled before its first use (the decode plan
- *    keeps one 32-bit completion counter per query at its start); every call
+ *    keeps one 32-bit completion counter per query at its start, the prefill
+ *    plan with key splits one per block of 8 queries, 4 when k_top > 512);
+ *    every call
  *    that completes leaves those counters at zero again, so a workspace is
  *    zeroed once and then reused freely, also from a captured HIP graph.
  */

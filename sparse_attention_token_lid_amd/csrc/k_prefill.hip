@@ -82,6 +82,52 @@ __device__ __forceinline__ float lane_select(uint64_t m, float a, float b) {
   return r;
 }
 
+// The k_top best of the P sorted split lists of one query (row t of
+// a.lists: P lists of K keys, descending, 0 = empty), merged by one wavefront
+// in registers and written as the output row.  N = 64 E >= K entries per
+// run, lane L holding elements E L .. E L + E - 1.  Two sorted runs merge in
+// one step: the N largest of runs A and B are max(A[i], B[N - 1 - i]), a
+// bitonic sequence, which the last log2(N) stages of the bitonic network
+// sort.  The lists were written by other workgroups, possibly on other XCDs:
+// they are read with agent-scope atomic loads, which bypass the caches that
+// are not coherent between XCDs.
+template <int E>
+__device__ __forceinline__ void wave_merge_lists(const KArgs& a, int64_t t) {
+  constexpr int N = kWave * E;
+  const int lane = lane_id();
+  const int P = a.P, K = a.K;
+  const uint64_t* lists = a.lists + (size_t)t * P * K;
+  auto load = [&](int p, bool reversed, uint64_t (&x)[E]) {
+    const uint64_t* l = lists + (size_t)p * K;
+#pragma unroll
+    for (int s = 0; s < E; ++s) {
+      const int e = E * lane + s;
+      const int j = reversed ? N - 1 - e : e;
+      x[s] = j < K ? __hip_atomic_load(l + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    }
+  };
+  uint64_t acc[E], nxt[E];
+  load(0, false, acc);
+  load(1, true, nxt);
+  for (int p = 1; p < P; ++p) {
+    uint64_t cur[E];
+#pragma unroll
+    for (int s = 0; s < E; ++s) cur[s] = nxt[s];
+    if (p + 1 < P) load(p + 1, true, nxt);
+#pragma unroll
+    for (int s = 0; s < E; ++s) acc[s] = acc[s] > cur[s] ? acc[s] : cur[s];
+    wave_bitonic_merge_reg<E, N, N / 2>(acc, lane);
+  }
+#pragma unroll
+  for (int s = 0; s < E; ++s) {
+    const int e = E * lane + s;
+    if (e < K) {
+      a.idx[t * K + e] = key_index(acc[s]);
+      if (a.score) a.score[t * K + e] = key_score(acc[s]);
+    }
+  }
+}
+
 template <int NW, int DT, bool MK>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   using M = Mfma<DT>;
@@ -97,6 +143,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   int64_t* rlo = reinterpret_cast<int64_t*>(hist + NW * 256);
   int64_t* rhi = rlo + NW;
   uint32_t* cflag = reinterpret_cast<uint32_t*>(rhi + NW);  // [2][NW] compaction requests
+  uint32_t& s_last = cflag[2 * NW];  // this workgroup is the last of its query block to finish
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int lane = threadIdx.x & (kWave - 1);
@@ -438,10 +485,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
 
   if (has_q) {
     wave_topk_finish(st);
-    if (P == 1)
+    if (P == 1) {
       wave_write_row(st.buf, a.K, a.idx + t * a.K, a.score ? a.score + t * a.K : nullptr, nullptr);
-    else
+    } else if (!a.fuse) {
       wave_write_row(st.buf, a.K, nullptr, nullptr, a.lists + ((size_t)t * P + p) * a.K);
+    } else {
+      uint64_t* out = a.lists + ((size_t)t * P + p) * a.K;
+      for (int i = lane; i < a.K; i += kWave)
+        __hip_atomic_store(out + i, st.buf[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (P > 1 && a.fuse) {
+    // Publish this split's lists, then let the last workgroup of the query
+    // block merge them: every store has completed (vmcnt(0)) before the
+    // workgroup's barrier and the counter increment (agent scope, wrapping at
+    // P, so it is back at zero after the launch).
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_last = __builtin_amdgcn_atomic_inc32(a.counters + qb, (unsigned)(P - 1), __ATOMIC_RELAXED, "agent") ==
+                       (unsigned)(P - 1) ? 1u : 0u;
+    __syncthreads();
+    if (s_last && has_q) {
+      const int n2 = next_pow2(a.K);
+      if (n2 == 256) wave_merge_lists<4>(a, t);
+      else if (n2 == 512) wave_merge_lists<8>(a, t);
+      else wave_merge_lists<16>(a, t);
+    }
   }
 }
 
@@ -465,7 +535,7 @@ hipError_t launch_one(const KArgs& a, hipStream_t st) {
 
 // dynamic part only; the two key tiles (2 x 32 KiB) are static LDS
 size_t prefill_lds_bytes(int nw, int cap) {
-  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 8 + 2 * (size_t)nw * 4;
+  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 8 + 2 * (size_t)nw * 4 + 16;
 }
 
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {

@@ -28,6 +28,7 @@ struct Plan {
   int keys_per_wg;  // decode: LDS key slots per workgroup
   int ch;           // merge: entries per list per round
   bool raw;         // decode: raw-score form (the last workgroup selects from all scores)
+  bool fuse;        // prefill, P > 1: the scoring kernel merges the split lists itself
   int64_t raw_ld;   // decode, raw form: scores per query row
   size_t ws;        // workspace bytes
   size_t ws_data;   // decode: offset of lists / raw scores (after the counters)
@@ -101,6 +102,19 @@ int make_plan(const lid_shape* s, Plan* pl) {
     pl->P = P;
     if (prefill_lds_bytes(pl->nw, pl->cap) + 2 * (size_t)kPrefillTile * kMfmaDim * 2 > kMaxLds)
       return LID_ERR_UNSUPPORTED;
+    if (P > 1) {
+      // workspace: per-query-block counters (zero between launches), then the
+      // split lists; with few splits the last workgroup of a query block
+      // merges them (the register merge needs next_pow2(K) in 256..1024)
+      const int n2 = next_pow2(K);
+      pl->fuse = P <= kFuseMaxSplits && n2 >= 256 && n2 <= 1024;
+      pl->ws_data = (size_t)cdiv(cdiv(s->n_tok, pl->nw) * 4, 256) * 256;
+      pl->ws = pl->ws_data + (size_t)s->n_tok * P * K * sizeof(uint64_t);
+      if (!pl->fuse) {
+        pl->ch = merge_chunk(P, K);
+        if (merge_lds_bytes(P, K, pl->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
+      }
+    }
   } else {  // decode
     int P = s->splits;
     if (!P) {
@@ -126,7 +140,7 @@ int make_plan(const lid_shape* s, Plan* pl) {
       pl->ws = pl->ws_data + (P > 1 ? (size_t)s->n_tok * P * K * sizeof(uint64_t) : 0);
     }
   }
-  if (pl->P > 1 && kind != LID_PLAN_DECODE) {
+  if (pl->P > 1 && kind == LID_PLAN_GENERIC) {
     pl->ch = merge_chunk(pl->P, K);
     if (merge_lds_bytes(pl->P, K, pl->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
     pl->ws = (size_t)s->n_tok * pl->P * K * sizeof(uint64_t);
@@ -183,7 +197,7 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   a.idx = idx;
   a.score = score;
   a.lists = reinterpret_cast<uint64_t*>(workspace);
-  if (pl.kind == LID_PLAN_DECODE) {
+  if (pl.kind == LID_PLAN_DECODE || (pl.kind == LID_PLAN_PREFILL && pl.P > 1)) {
     a.counters = reinterpret_cast<uint32_t*>(workspace);
     unsigned char* data = reinterpret_cast<unsigned char*>(workspace) + pl.ws_data;
     a.lists = reinterpret_cast<uint64_t*>(data);
@@ -199,6 +213,7 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   a.P = pl.P;
   a.cap = pl.cap;
   a.dtype = s.qk_dtype;
+  a.fuse = pl.fuse ? 1 : 0;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   hipError_t e;
@@ -208,7 +223,7 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   else e = launch_generic(a, st);
   if (e != hipSuccess) return hip_fail(e);
   if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
-  if (pl.P > 1 && pl.kind != LID_PLAN_DECODE) {
+  if (pl.P > 1 && pl.kind != LID_PLAN_DECODE && !pl.fuse) {
     e = launch_merge(a, pl.ch, st);
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -17,11 +17,13 @@ struct KArgs {
   float* score;             // [n_tok, K], or null
   uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1)
   uint32_t* raw;            // decode, raw form: [n_tok, raw_ld] ordered scores (0 = no key)
-  uint32_t* counters;       // decode: [n_tok] finished-workgroup counters (zero between launches)
+  uint32_t* counters;       // finished-workgroup counters (zero between launches): decode [n_tok],
+                            // prefill with a fused finish [query blocks]
   int64_t n_tok, n_kv, mask_ld, raw_ld;
   int32_t H, D, K, P;
   int32_t cap;              // per-wave candidate buffer capacity (entries)
   int32_t dtype;            // 0 f32, 1 f16, 2 bf16
+  int32_t fuse;             // prefill, P > 1: the last workgroup of a query block merges its lists
 };
 
 // Shapes the MFMA kernels are written for.
@@ -30,6 +32,7 @@ constexpr int kMfmaDim = 128;
 constexpr int kPrefillTile = 128;      // keys per LDS tile
 constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
 constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
+constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);

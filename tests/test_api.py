@@ -67,8 +67,14 @@ def test_auto_plans_and_workspace(L, name, plan):
         span = -(-wl.n_kv // 32) * 32
         raw = wl.n_tok * (-(-span // 64) * 64) * 4
         assert ws == counters + (raw if span <= 32768 else lists)
+    elif splits > 1:
+        # per-query-block counters (8 queries per block at k_top <= 512),
+        # then the split lists
+        nw = 8 if wl.k_top <= 512 else 4
+        counters = -(-(-(-wl.n_tok // nw)) * 4 // 256) * 256
+        assert ws == counters + lists
     else:
-        assert ws == lists
+        assert ws == 0
     # O(n_tok * k_top * splits) with splits <= 256, whatever n_kv is
     assert splits <= 256 and ws <= 256 * -(-wl.n_tok * 4 // 256) + wl.n_tok * wl.k_top * 8 * 256
     if wl.n_kv >= 131072:
