@@ -269,7 +269,75 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The same cut with the buffer read once into registers (R per lane, entry
+// lane + 64 r in x[r]): the AND/OR statistics, the radix passes (8-bit
+// digits counted into the wave's LDS histogram), the minimum of the selected
+// keys and the compaction all work on the registers, so the buffer is read
+// once and written once.  Needs cap <= 64 R.
+template <int R>
+__device__ __forceinline__ void wave_topk_reduce_reg(WaveTopK& st) {
+  const int lane = lane_id();
+  const int n = st.count;
+  uint64_t x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = (lane + kWave * r < n) ? st.buf[lane + kWave * r] : 0ull;
+  uint64_t an = ~0ull, on = 0ull;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    an &= x[r] ? x[r] : ~0ull;
+    on |= x[r];
+  }
+  an = uniform_u64(wave_and_u64(an));
+  on = uniform_u64(wave_or_u64(on));
+  uint64_t kap = an;  // all keys equal (n == 1): that key
+  if (an != on) {
+    const int top = 63 - __clzll((long long)(an ^ on));
+    uint64_t pmask = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
+    uint64_t prefix = an & pmask;
+    uint32_t need = (uint32_t)st.K;
+    int shift = top - 7;
+    for (;;) {
+      const int sh = shift > 0 ? shift : 0;
+#pragma unroll
+      for (int i = 0; i < 256 / kWave; ++i) st.hist[lane + kWave * i] = 0u;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (x[r] && (x[r] & pmask) == prefix) atomicAdd(&st.hist[(uint32_t)(x[r] >> sh) & 0xFFu], 1u);
+      __builtin_amdgcn_wave_barrier();
+      const DigitPick pk = pick_digit(st.hist, need);
+      need -= pk.above;
+      prefix |= (uint64_t)pk.d << sh;
+      pmask |= 0xFFull << sh;
+      if (pk.cnt == need || sh == 0) break;
+      shift -= 8;
+    }
+    // the selected keys are those >= prefix (exactly K); the K-th is their minimum
+    uint64_t mn = ~0ull;
+#pragma unroll
+    for (int r = 0; r < R; ++r) mn = (x[r] != 0ull && x[r] >= prefix && x[r] < mn) ? x[r] : mn;
+    kap = uniform_u64(wave_min_u64(mn));
+  }
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool keep = x[r] != 0ull && x[r] >= kap;
+    const uint64_t m = ballot(keep);
+    if (keep) st.buf[base + mbcnt(m)] = x[r];
+    base += __popcll(m);
+  }
+  st.count = __builtin_amdgcn_readfirstlane(base);
+  st.tau = kap;
+  st.tau_v = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(key_score(kap))));
+}
+
+constexpr int kReduceRegRows = 19;  // register cut for buffers of up to 1216 entries (k_top <= 512)
+
 __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
+  if (st.count > st.K && st.cap <= kWave * kReduceRegRows) {
+    wave_topk_reduce_reg<kReduceRegRows>(st);
+    return;
+  }
   if (st.count > st.K) {
     const uint64_t kap = uniform_u64(wave_kth_largest(st.buf, st.count, st.K, st.hist));
     st.count = __builtin_amdgcn_readfirstlane(wave_compact(st.buf, st.count, kap));
