@@ -97,26 +97,40 @@ __device__ __forceinline__ void wave_merge_lists(const KArgs& a, int64_t t) {
   const int lane = lane_id();
   const int P = a.P, K = a.K;
   const uint64_t* lists = a.lists + (size_t)t * P * K;
+  // 16-byte loads through a buffer resource (entries past K read as 0; K is
+  // even, so no load straddles the end) with the cache policy of an
+  // agent-scope atomic load (sc1).  Lane L reads its E entries E L ..
+  // E L + E - 1, or for a reversed run the entries N - E (L + 1) ..
+  // N - 1 - E L in reverse order.
   auto load = [&](int p, bool reversed, uint64_t (&x)[E]) {
-    const uint64_t* l = lists + (size_t)p * K;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint64_t*>(lists + (size_t)p * K), (short)0, K * 8, 0x00020000);
+    const int j0 = reversed ? E * (kWave - 1 - lane) : E * lane;
 #pragma unroll
-    for (int s = 0; s < E; ++s) {
-      const int e = E * lane + s;
-      const int j = reversed ? N - 1 - e : e;
-      x[s] = j < K ? __hip_atomic_load(l + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    for (int c = 0; c < E / 2; ++c) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (j0 + 2 * c) * 8, 0, 16));
+      const uint64_t e0 = ((uint64_t)v[1] << 32) | v[0], e1 = ((uint64_t)v[3] << 32) | v[2];
+      if (reversed) { x[E - 1 - 2 * c] = e0; x[E - 2 - 2 * c] = e1; }
+      else { x[2 * c] = e0; x[2 * c + 1] = e1; }
     }
   };
-  uint64_t acc[E], nxt[E];
+  // all loads of a batch of up to 8 runs are in flight before its merges
+  constexpr int B = E >= 16 ? 4 : 8;
+  uint64_t acc[E];
   load(0, false, acc);
-  load(1, true, nxt);
-  for (int p = 1; p < P; ++p) {
-    uint64_t cur[E];
+  for (int p0 = 1; p0 < P; p0 += B) {
+    uint64_t run[B][E];
 #pragma unroll
-    for (int s = 0; s < E; ++s) cur[s] = nxt[s];
-    if (p + 1 < P) load(p + 1, true, nxt);
+    for (int b = 0; b < B; ++b)
+      if (p0 + b < P) load(p0 + b, true, run[b]);
 #pragma unroll
-    for (int s = 0; s < E; ++s) acc[s] = acc[s] > cur[s] ? acc[s] : cur[s];
-    wave_bitonic_merge_reg<E, N, N / 2>(acc, lane);
+    for (int b = 0; b < B; ++b) {
+      if (p0 + b < P) {
+#pragma unroll
+        for (int s = 0; s < E; ++s) acc[s] = acc[s] > run[b][s] ? acc[s] : run[b][s];
+        wave_bitonic_merge_reg<E, N, N / 2>(acc, lane);
+      }
+    }
   }
 #pragma unroll
   for (int s = 0; s < E; ++s) {
@@ -126,6 +140,35 @@ __device__ __forceinline__ void wave_merge_lists(const KArgs& a, int64_t t) {
       if (a.score) a.score[t * K + e] = key_score(acc[s]);
     }
   }
+}
+
+// The k_top best of the P unsorted split lists of one query (row t of
+// a.lists: P x K keys, 0 = empty; P K <= 64 R), by one wavefront: all keys
+// are read into registers at once (16-byte agent-coherent loads as above),
+// the K-th largest is found by radix passes over the registers, the K best
+// are compacted into the wave's LDS buffer, sorted there through registers
+// and written as the output row.
+template <int R, int E>
+__device__ __forceinline__ void wave_select_lists(const KArgs& a, int64_t t, WaveTopK& st) {
+  const int lane = lane_id();
+  const int n = a.P * a.K;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint64_t*>(a.lists + (size_t)t * n), (short)0, n * 8, 0x00020000);
+  uint64_t x[R];
+#pragma unroll
+  for (int c = 0; c < R / 2; ++c) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + kWave * c) * 16, 0, 16));
+    x[2 * c] = ((uint64_t)v[1] << 32) | v[0];
+    x[2 * c + 1] = ((uint64_t)v[3] << 32) | v[2];
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) c += x[r] ? 1u : 0u;
+  const uint32_t present = __builtin_amdgcn_readfirstlane(wave_sum_u32(c));
+  const uint64_t kap = present > (uint32_t)a.K ? wave_cut_reg<R, true>(x, (uint32_t)a.K, st.hist) : 1ull;
+  const int m = wave_compact_reg<R>(x, kap, st.buf);
+  wave_sort_desc_reg<E>(st.buf, m);
+  wave_write_row(st.buf, a.K, a.idx + t * a.K, a.score ? a.score + t * a.K : nullptr, nullptr);
 }
 
 template <int NW, int DT, bool MK>
@@ -149,8 +192,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int G = lane >> 4, r16 = lane & 15;
   const int P = a.P;
-  const int p = (int)(blockIdx.x % (unsigned)P);
-  const int64_t qb = blockIdx.x / (unsigned)P;
+  // Workgroups go to the 8 XCDs round-robin (block b to XCD b % 8).  The
+  // (query block, split) pairs are numbered so that each XCD gets a
+  // contiguous run of them: the P splits of a query block share one XCD and
+  // its L2, which then fetches their queries from HBM once, not P times.
+  uint32_t g = blockIdx.x;
+  if (P > 1) {
+    const uint32_t T = gridDim.x, x = blockIdx.x % 8u, i = blockIdx.x / 8u;
+    const uint32_t Q = T / 8u, Rm = T % 8u;
+    g = x * Q + (x < Rm ? x : Rm) + i;
+  }
+  const int p = (int)(g % (unsigned)P);
+  const int64_t qb = g / (unsigned)P;
   const int64_t t = qb * NW + wv;
   const bool has_q = t < a.n_tok;
 
@@ -364,7 +417,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // 128 free slots remain (rare once the stream is long).
   auto room = [&]() {
     st.count = __builtin_amdgcn_readfirstlane(st.count);  // keep it scalar (see uniform_u64)
-    if (st.count > st.cap - 2 * kWave) wave_topk_reduce(st);
+    if (st.count > st.cap - 2 * kWave) wave_topk_trim(st);
   };
   // Compactions are synchronised across the workgroup: a wave that could not
   // take a whole further tile (two units) raises its flag before the tile
@@ -382,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     for (int w2 = 0; w2 < NW; ++w2) any |= cflag[(it & 1) * NW + w2];
     if (__builtin_amdgcn_readfirstlane(any)) {
       st.count = __builtin_amdgcn_readfirstlane(st.count);
-      wave_topk_reduce(st);
+      wave_topk_trim(st);
     }
   };
 
@@ -483,7 +536,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     for (int i = 0; i < 8; ++i) insert_slice(u1, i, z);
   }
 
-  if (has_q) {
+  if (has_q && a.fuse == 2) {
+    // unsorted split list: the K best (all present keys if fewer), 0-padded
+    wave_topk_reduce(st);
+    uint64_t* out = a.lists + ((size_t)t * P + p) * a.K;
+    for (int i = lane; i < a.K; i += kWave)
+      __hip_atomic_store(out + i, i < st.count ? st.buf[i] : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (has_q) {
     wave_topk_finish(st);
     if (P == 1) {
       wave_write_row(st.buf, a.K, a.idx + t * a.K, a.score ? a.score + t * a.K : nullptr, nullptr);
@@ -508,9 +567,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     __syncthreads();
     if (s_last && has_q) {
       const int n2 = next_pow2(a.K);
-      if (n2 == 256) wave_merge_lists<4>(a, t);
-      else if (n2 == 512) wave_merge_lists<8>(a, t);
-      else wave_merge_lists<16>(a, t);
+      if (a.fuse == 2) {
+        if (n2 == 256) wave_select_lists<kFuseSelectRows, 4>(a, t, st);
+        else if (n2 == 512) wave_select_lists<kFuseSelectRows, 8>(a, t, st);
+        else wave_select_lists<kFuseSelectRows, 16>(a, t, st);
+      } else {
+        if (n2 == 256) wave_merge_lists<4>(a, t);
+        else if (n2 == 512) wave_merge_lists<8>(a, t);
+        else wave_merge_lists<16>(a, t);
+      }
     }
   }
 }

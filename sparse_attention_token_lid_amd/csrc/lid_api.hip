@@ -28,7 +28,8 @@ struct Plan {
   int keys_per_wg;  // decode: LDS key slots per workgroup
   int ch;           // merge: entries per list per round
   bool raw;         // decode: raw-score form (the last workgroup selects from all scores)
-  bool fuse;        // prefill, P > 1: the scoring kernel merges the split lists itself
+  int fuse;         // prefill, P > 1: the scoring kernel finishes from the split lists itself
+                    // (1: merging sorted lists, 2: selecting from unsorted ones)
   int64_t raw_ld;   // decode, raw form: scores per query row
   size_t ws;        // workspace bytes
   size_t ws_data;   // decode: offset of lists / raw scores (after the counters)
@@ -105,9 +106,11 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (P > 1) {
       // workspace: per-query-block counters (zero between launches), then the
       // split lists; with few splits the last workgroup of a query block
-      // merges them (the register merge needs next_pow2(K) in 256..1024)
+      // merges them (the register merge needs next_pow2(K) in 256..1024 and an
+      // even K)
       const int n2 = next_pow2(K);
-      pl->fuse = P <= kFuseMaxSplits && n2 >= 256 && n2 <= 1024;
+      const bool fusable = P <= kFuseMaxSplits && n2 >= 256 && n2 <= 1024 && K % 2 == 0;
+      pl->fuse = !fusable ? 0 : ((int64_t)P * K <= 64 * kFuseSelectRows ? 2 : 1);
       pl->ws_data = (size_t)cdiv(cdiv(s->n_tok, pl->nw) * 4, 256) * 256;
       pl->ws = pl->ws_data + (size_t)s->n_tok * P * K * sizeof(uint64_t);
       if (!pl->fuse) {
@@ -213,7 +216,7 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   a.P = pl.P;
   a.cap = pl.cap;
   a.dtype = s.qk_dtype;
-  a.fuse = pl.fuse ? 1 : 0;
+  a.fuse = pl.fuse;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   hipError_t e;

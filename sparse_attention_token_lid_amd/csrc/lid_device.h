@@ -273,14 +273,19 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 // lane + 64 r in x[r]): the AND/OR statistics, the radix passes (8-bit
 // digits counted into the wave's LDS histogram), the minimum of the selected
 // keys and the compaction all work on the registers, so the buffer is read
-// once and written once.  Needs cap <= 64 R.
-template <int R>
-__device__ __forceinline__ void wave_topk_reduce_reg(WaveTopK& st) {
+// once and written once.  Needs cap <= 64 R.  EXACT = false is the cheaper
+// trim used while the stream runs: the passes stop as soon as keeping the
+// whole bucket that holds the K-th key keeps at most kTrimSlack keys beyond K,
+// and the threshold becomes that bucket's floor (still <= the K-th key, so
+// nothing that can reach the final top-K is dropped).
+constexpr int kTrimSlack = 64;
+// Threshold of the K best among the nonzero keys x (R per lane, unique),
+// which must number more than K: the K-th largest key (EXACT), or the floor
+// of the 8-bit radix bucket that holds it once that bucket adds at most
+// kTrimSlack keys beyond K (!EXACT).  hist: the wave's 256-bin LDS histogram.
+template <int R, bool EXACT>
+__device__ __forceinline__ uint64_t wave_cut_reg(const uint64_t (&x)[R], uint32_t K, uint32_t* hist) {
   const int lane = lane_id();
-  const int n = st.count;
-  uint64_t x[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) x[r] = (lane + kWave * r < n) ? st.buf[lane + kWave * r] : 0ull;
   uint64_t an = ~0ull, on = 0ull;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -289,44 +294,60 @@ __device__ __forceinline__ void wave_topk_reduce_reg(WaveTopK& st) {
   }
   an = uniform_u64(wave_and_u64(an));
   on = uniform_u64(wave_or_u64(on));
-  uint64_t kap = an;  // all keys equal (n == 1): that key
-  if (an != on) {
-    const int top = 63 - __clzll((long long)(an ^ on));
-    uint64_t pmask = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
-    uint64_t prefix = an & pmask;
-    uint32_t need = (uint32_t)st.K;
-    int shift = top - 7;
-    for (;;) {
-      const int sh = shift > 0 ? shift : 0;
+  if (an == on) return an;  // a single key
+  const int top = 63 - __clzll((long long)(an ^ on));
+  uint64_t pmask = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
+  uint64_t prefix = an & pmask;
+  uint32_t need = K;
+  int shift = top - 7;
+  for (;;) {
+    const int sh = shift > 0 ? shift : 0;
 #pragma unroll
-      for (int i = 0; i < 256 / kWave; ++i) st.hist[lane + kWave * i] = 0u;
-      __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < 256 / kWave; ++i) hist[lane + kWave * i] = 0u;
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (x[r] && (x[r] & pmask) == prefix) atomicAdd(&st.hist[(uint32_t)(x[r] >> sh) & 0xFFu], 1u);
-      __builtin_amdgcn_wave_barrier();
-      const DigitPick pk = pick_digit(st.hist, need);
-      need -= pk.above;
-      prefix |= (uint64_t)pk.d << sh;
-      pmask |= 0xFFull << sh;
-      if (pk.cnt == need || sh == 0) break;
-      shift -= 8;
-    }
-    // the selected keys are those >= prefix (exactly K); the K-th is their minimum
-    uint64_t mn = ~0ull;
-#pragma unroll
-    for (int r = 0; r < R; ++r) mn = (x[r] != 0ull && x[r] >= prefix && x[r] < mn) ? x[r] : mn;
-    kap = uniform_u64(wave_min_u64(mn));
+    for (int r = 0; r < R; ++r)
+      if (x[r] && (x[r] & pmask) == prefix) atomicAdd(&hist[(uint32_t)(x[r] >> sh) & 0xFFu], 1u);
+    __builtin_amdgcn_wave_barrier();
+    const DigitPick pk = pick_digit(hist, need);
+    need -= pk.above;
+    prefix |= (uint64_t)pk.d << sh;
+    pmask |= 0xFFull << sh;
+    if (pk.cnt == need || sh == 0) break;
+    if (!EXACT && pk.cnt - need <= (uint32_t)kTrimSlack) return prefix;  // the bucket's floor
+    shift -= 8;
   }
+  // the selected keys are those >= prefix (exactly K); the K-th is their minimum
+  uint64_t mn = ~0ull;
+#pragma unroll
+  for (int r = 0; r < R; ++r) mn = (x[r] != 0ull && x[r] >= prefix && x[r] < mn) ? x[r] : mn;
+  return uniform_u64(wave_min_u64(mn));
+}
+
+// The nonzero keys >= kap of x (R per lane) into buf[0..), any order; returns
+// how many (wave-uniform).
+template <int R>
+__device__ __forceinline__ int wave_compact_reg(const uint64_t (&x)[R], uint64_t kap, uint64_t* buf) {
   int base = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const bool keep = x[r] != 0ull && x[r] >= kap;
     const uint64_t m = ballot(keep);
-    if (keep) st.buf[base + mbcnt(m)] = x[r];
+    if (keep) buf[base + mbcnt(m)] = x[r];
     base += __popcll(m);
   }
-  st.count = __builtin_amdgcn_readfirstlane(base);
+  return __builtin_amdgcn_readfirstlane(base);
+}
+
+template <int R, bool EXACT>
+__device__ __forceinline__ void wave_topk_reduce_reg(WaveTopK& st) {
+  const int lane = lane_id();
+  const int n = st.count;
+  uint64_t x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = (lane + kWave * r < n) ? st.buf[lane + kWave * r] : 0ull;
+  const uint64_t kap = wave_cut_reg<R, EXACT>(x, (uint32_t)st.K, st.hist);
+  st.count = wave_compact_reg<R>(x, kap, st.buf);
   st.tau = kap;
   st.tau_v = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(key_score(kap))));
 }
@@ -335,7 +356,7 @@ constexpr int kReduceRegRows = 19;  // register cut for buffers of up to 1216 en
 
 __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
   if (st.count > st.K && st.cap <= kWave * kReduceRegRows) {
-    wave_topk_reduce_reg<kReduceRegRows>(st);
+    wave_topk_reduce_reg<kReduceRegRows, true>(st);
     return;
   }
   if (st.count > st.K) {
@@ -344,6 +365,17 @@ __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
     st.tau = kap;
     st.tau_v = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(key_score(kap))));
   }
+}
+
+// Cut the buffer to between K and K + kTrimSlack keys (all keys that can still
+// reach the final top-K stay): the cheaper cut for compactions inside the
+// stream; the final one uses wave_topk_reduce.
+__device__ __forceinline__ void wave_topk_trim(WaveTopK& st) {
+  if (st.cap <= kWave * kReduceRegRows) {
+    if (st.count > st.K + kTrimSlack) wave_topk_reduce_reg<kReduceRegRows, false>(st);
+    return;
+  }
+  wave_topk_reduce(st);
 }
 
 // Offer one key per lane (valid == false: no candidate on this lane).

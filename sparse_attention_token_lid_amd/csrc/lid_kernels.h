@@ -23,7 +23,9 @@ struct KArgs {
   int32_t H, D, K, P;
   int32_t cap;              // per-wave candidate buffer capacity (entries)
   int32_t dtype;            // 0 f32, 1 f16, 2 bf16
-  int32_t fuse;             // prefill, P > 1: the last workgroup of a query block merges its lists
+  int32_t fuse;             // prefill, P > 1: the last workgroup of a query block finishes the
+                            // query's top-k from the split lists: 1 = sorted lists merged,
+                            // 2 = unsorted lists selected from (P K <= 64 kFuseSelectRows)
 };
 
 // Shapes the MFMA kernels are written for.
@@ -33,6 +35,7 @@ constexpr int kPrefillTile = 128;      // keys per LDS tile
 constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
 constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
+constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <= 64 x this keys
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);
