@@ -422,6 +422,34 @@ __host__ __device__ constexpr int next_pow2(int x) {
 // at element distance j < E stays inside one lane's registers; one at
 // distance j >= E pairs lanes L and L ^ (j / E), exchanged with DPP or a
 // permlane swap.  No LDS and no barrier; E independent chains per stage.
+// Lane exchange for the paired compare-exchange below: lanes with
+// (lane & D) == 0 end up holding slot s's pair (own element in a, partner in
+// b), the others slot t's pair (partner in a, own element in b), and the same
+// call applied to the results puts every element back.  D = 16 and 32 use
+// the permlane swaps; D = 4 and 8 two bank-masked DPP moves (the banks of 4
+// lanes with bit D set, resp. clear, take the row-shifted value).
+template <int D>
+__device__ __forceinline__ void pair_exchange(uint32_t& a, uint32_t& b) {
+  if constexpr (D == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  } else if constexpr (D == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  } else {
+    static_assert(D == 4 || D == 8, "paired exchange distance");
+    constexpr int kShr = D == 4 ? 0x114 : 0x118;  // row_shr:D (lane L reads L - D)
+    constexpr int kShl = D == 4 ? 0x104 : 0x108;  // row_shl:D (lane L reads L + D)
+    constexpr int kHi = D == 4 ? 0xA : 0xC;       // banks whose lanes have bit D set
+    const uint32_t a2 = (uint32_t)__builtin_amdgcn_update_dpp((int)a, (int)b, kShr, 0xF, kHi, false);
+    const uint32_t b2 = (uint32_t)__builtin_amdgcn_update_dpp((int)b, (int)a, kShl, 0xF, 0xF ^ kHi, false);
+    a = a2;
+    b = b2;
+  }
+}
+
 template <int E, int K, int J>
 __device__ __forceinline__ void wave_bitonic_stage_reg(uint64_t (&x)[E], int lane) {
   if constexpr (J < E) {
@@ -432,9 +460,33 @@ __device__ __forceinline__ void wave_bitonic_stage_reg(uint64_t (&x)[E], int lan
       if constexpr (K < E) desc = (s & K) == 0;
       else desc = (lane & (K / E)) == 0;
       const uint64_t a = x[s], b = x[s | J];
-      const bool sw = desc ? (a < b) : (a > b);
+      const bool sw = (a < b) == desc;  // equal keys (empty slots) need no swap
       x[s] = sw ? b : a;
       x[s | J] = sw ? a : b;
+    }
+  } else if constexpr (E >= 2 && (J / E == 4 || J / E == 8 || J / E == 16 || J / E == 32)) {
+    // slots s and s + E / 2 travel together: one exchange gathers both
+    // elements of a pair in one lane, which compare-exchanges them in
+    // registers, and the same exchange returns them
+    constexpr int D = J / E;
+#pragma unroll
+    for (int s = 0; s < E / 2; ++s) {
+      uint32_t alo = (uint32_t)x[s], ahi = (uint32_t)(x[s] >> 32);
+      uint32_t blo = (uint32_t)x[s + E / 2], bhi = (uint32_t)(x[s + E / 2] >> 32);
+      pair_exchange<D>(alo, blo);
+      pair_exchange<D>(ahi, bhi);
+      const uint64_t a = ((uint64_t)ahi << 32) | alo, b = ((uint64_t)bhi << 32) | blo;  // lower, upper element
+      bool desc;  // K >= 2 J >= 2 E here: the direction follows the lower element's lane
+      if constexpr (K / E >= kWave) desc = true;
+      else desc = (lane & (K / E)) == 0;
+      const bool sw = (a < b) == desc;
+      const uint64_t a2 = sw ? b : a, b2 = sw ? a : b;
+      alo = (uint32_t)a2; ahi = (uint32_t)(a2 >> 32);
+      blo = (uint32_t)b2; bhi = (uint32_t)(b2 >> 32);
+      pair_exchange<D>(alo, blo);
+      pair_exchange<D>(ahi, bhi);
+      x[s] = ((uint64_t)ahi << 32) | alo;
+      x[s + E / 2] = ((uint64_t)bhi << 32) | blo;
     }
   } else {
     constexpr int D = J / E;
