@@ -64,6 +64,7 @@ constexpr int kRows = kRawMax / BS;   // positions per thread in the raw selecti
 constexpr int kDigitBits = 11;        // radix digit of the raw selection
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kCandMax = 4096;        // candidates gathered into LDS for the exact select
+static_assert(kCandMax == 8 * kTreeCap, "the merge tree takes up to 8 chunks of kTreeCap candidates");
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * D + ((ch ^ (row & 15)) << 3); }
 
@@ -155,22 +156,38 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
   }
   const uint32_t present = block_sum_u32(c, red);
 
+  // Candidates are the values >= thr (thr >= 1, so only present ones); the
+  // gather writes them wave by wave: wcount[] holds each wave's count for
+  // the threshold in wthr, and the waves' offsets follow from it.
+  uint32_t* wcount = red + 4 * NW;  // [NW]
+  auto count_waves = [&](uint32_t th) -> uint32_t {  // block total; wcount[] filled
+    opaque();
+    uint32_t c2 = 0;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) c2 += (uint32_t)__popcll(ballot(v[r] >= th));
+    if (lane_id() == 0) wcount[wv] = c2;
+    __syncthreads();
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) tot += wcount[w2];
+    return tot;
+  };
   uint32_t thr = 1u;        // candidates: v >= thr
   bool tie_path = false;    // the k_top-th score is shared by too many positions
   bool have_thr = present <= (uint32_t)K;  // then every present value is a candidate
+  bool counted = false;     // wcount[] holds the counts for thr
   if (!have_thr) {
     // Lower bound of the k_top-th score: the k_top-th largest of the
     // per-thread top-2 values (k_top of them are >= it, and it is one of the
     // values); it usually leaves a few hundred candidates.
     const uint32_t top2[2] = {m1, m2};
     const uint32_t lb = block_kth_largest_reg<uint32_t, 2>(top2, (uint32_t)K, hw, sh, red);
-    opaque();
-    uint32_t cc = 0;
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) cc += v[r] >= lb ? 1u : 0u;
-    if (block_sum_u32(cc, red) <= (uint32_t)kCandMax) {
+    if (count_waves(lb) <= (uint32_t)kCandMax) {
       thr = lb;
       have_thr = true;
+      counted = true;
+    } else {
+      __syncthreads();  // wcount[] is read by every wave before it is reused
     }
   }
   if (!have_thr) {
@@ -260,21 +277,31 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
 
   // gather the candidates as 64-bit keys (score word, ~index)
   int m = 0;
-  opaque();
   if (!tie_path) {
-    uint64_t bits = 0ull;  // slot r of this thread is a candidate
+    thr = thr > 1u ? thr : 1u;  // absent positions hold 0 and never qualify
+    const uint32_t total = counted ? [&] {
+      uint32_t tot = 0;
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) bits |= (uint64_t)((v[r] != 0u && v[r] >= thr) ? 1u : 0u) << r;
-    int total;
-    int pos = block_excl_scan(__popcll(bits), &total, *sh);
+      for (int w2 = 0; w2 < NW; ++w2) tot += wcount[w2];
+      return tot;
+    }() : count_waves(thr);
+    uint32_t base = 0;  // this wave's offset: the counts of the waves before it
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) base += w2 < wv ? wcount[w2] : 0u;
+    base = __builtin_amdgcn_readfirstlane(base);
+    opaque();
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-      if ((bits >> r) & 1ull) {
+      const bool c = v[r] >= thr;
+      const uint64_t mk = ballot(c);
+      if (c) {
         const uint32_t s = (uint32_t)(lo + raw_pos(r, tid));
-        cand[pos++] = ((uint64_t)v[r] << 32) | (uint64_t)(~s);
+        cand[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] =
+            ((uint64_t)v[r] << 32) | (uint64_t)(~s);
       }
+      base += (uint32_t)__popcll(mk);
     }
-    m = total;
+    m = (int)total;
   } else {
     // everything above thr, then the first `need` positions (in index order)
     // that score exactly thr: the cut position is found by bisection
@@ -307,6 +334,11 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
     m = gather([&](int r) { return v[r] == thr && raw_pos(r, tid) < x0; }, above);
   }
   __syncthreads();
+  if (next_pow2(K) == kTreeCap) {
+    // the digit histograms are free now: they hold the merge levels
+    block_topk_tree_any(cand, reinterpret_cast<uint64_t*>(hw), m, K, a.idx + t * K, a.score ? a.score + t * K : nullptr);
+    return;
+  }
   block_select_sorted_reg<kCandMax / BS>(cand, m, K, sel, tmp, hw, sh, red);
   for (int i = tid; i < K; i += BS) {
     a.idx[t * K + i] = key_index(sel[i]);

@@ -163,4 +163,118 @@ __device__ __forceinline__ void block_select_sorted_any(const uint64_t* arr, int
   block_sort_desc(sel, n2, tmp);
 }
 
+// ---------------------------------------------------------- merge-tree top-K
+// The K best (next_pow2(K) == kTreeCap) of buf[0..m), m <= 8 * 64 E, sorted
+// descending, by the block's 8 wavefronts without a radix select: each
+// wavefront sorts a chunk of 64 E keys in registers (wave_sort_reg), then
+// three levels merge pairs of sorted runs through LDS, one barrier each.
+// Two sorted runs A, B of length L give one bitonic sequence C: A followed by
+// B reversed when 2 L <= kTreeCap, else max(A[i], B[L - 1 - i]), which holds
+// the kTreeCap best of both.  The W wavefronts of a merge split its output
+// into W blocks: the first log2(W) half-cleaner stages of the bitonic merge
+// act on the columns C[i + u N / W], u < W, which each wavefront evaluates
+// straight from LDS, keeping the value of its own block; its block is then
+// bitonic and is sorted by the remaining stages in registers.  buf holds the
+// candidates (8 * 64 E entries, those at or past m read as empty) and alt is
+// LDS for 2048 more; the result goes straight to the output row.
+constexpr int kTreeCap = 512;
+
+template <int EB, int W, int LIN, bool CAPPED>
+__device__ __forceinline__ void wave_merge_block(const uint64_t* A, const uint64_t* B, int j, uint64_t (&x)[EB]) {
+  constexpr int NB = kWave * EB;  // outputs per wavefront
+  const int lane = lane_id();
+#pragma unroll
+  for (int s = 0; s < EB; ++s) {
+    uint64_t v[W];
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      const int i = u * NB + EB * lane + s;  // position in C
+      if constexpr (CAPPED) {
+        const uint64_t a = A[i], b = B[LIN - 1 - i];
+        v[u] = a > b ? a : b;
+      } else {
+        v[u] = i < LIN ? A[i] : B[2 * LIN - 1 - i];
+      }
+    }
+#pragma unroll
+    for (int h = W / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int u = 0; u < W; ++u)
+        if (!(u & h)) {
+          const uint64_t hi = v[u] > v[u + h] ? v[u] : v[u + h];
+          const uint64_t lo = v[u] > v[u + h] ? v[u + h] : v[u];
+          v[u] = hi;
+          v[u + h] = lo;
+        }
+    uint64_t r = v[0];
+#pragma unroll
+    for (int u = 1; u < W; ++u) r = j == u ? v[u] : r;
+    x[s] = r;
+  }
+  wave_bitonic_merge_reg<EB, NB, NB / 2>(x, lane);
+}
+
+// Level LVL (1..3): 8 >> LVL merges of the runs in src (length LIN, stride
+// SIN), W = 2^LVL wavefronts each, into dst (length LOUT, stride LOUT), or the
+// output row at the last level.
+template <int E, int LVL>
+__device__ __forceinline__ void tree_level(const uint64_t* src, uint64_t* dst, uint64_t* other, int K,
+                                           int32_t* idx_row, float* score_row) {
+  constexpr int CH = kWave * E;
+  constexpr int LIN = (CH << (LVL - 1)) < kTreeCap ? (CH << (LVL - 1)) : kTreeCap;
+  constexpr int SIN = LVL == 1 ? CH : LIN;
+  constexpr bool CAPPED = 2 * LIN > kTreeCap;
+  constexpr int LOUT = CAPPED ? kTreeCap : 2 * LIN;
+  constexpr int W = 1 << LVL;
+  constexpr int EB = LOUT / W / kWave;
+  static_assert(EB >= 1 && EB * kWave * W == LOUT, "block split");
+  const int wv = threadIdx.x / kWave, lane = lane_id();
+  const int g = wv / W, j = wv % W;
+  uint64_t x[EB];
+  wave_merge_block<EB, W, LIN, CAPPED>(src + (2 * g) * SIN, src + (2 * g + 1) * SIN, j, x);
+  if constexpr (LVL == 3) {
+#pragma unroll
+    for (int s = 0; s < EB; ++s) {
+      const int i = j * kWave * EB + EB * lane + s;
+      if (i < K) {
+        idx_row[i] = key_index(x[s]);
+        if (score_row) score_row[i] = key_score(x[s]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < EB; ++s) dst[g * LOUT + j * kWave * EB + EB * lane + s] = x[s];
+    __syncthreads();
+    tree_level<E, LVL + 1>(dst, other, dst, K, idx_row, score_row);
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void block_topk_tree(uint64_t* buf, uint64_t* alt, int m, int K, int32_t* idx_row,
+                                                float* score_row) {
+  static_assert(kSelThreads == 8 * kWave, "eight wavefronts");
+  constexpr int CH = kWave * E;
+  const int wv = threadIdx.x / kWave, lane = lane_id();
+  uint64_t x[E];
+#pragma unroll
+  for (int s = 0; s < E; ++s) {
+    const int i = wv * CH + E * lane + s;
+    x[s] = i < m ? buf[i] : 0ull;
+  }
+  wave_sort_reg<E>(x, lane);
+  // each wavefront rewrites only the chunk it read itself
+#pragma unroll
+  for (int s = 0; s < E; ++s) buf[wv * CH + E * lane + s] = x[s];
+  __syncthreads();
+  tree_level<E, 1>(buf, alt, buf, K, idx_row, score_row);
+}
+
+// Dispatch on m (block-uniform): the smallest chunk that holds m / 8.
+__device__ __forceinline__ void block_topk_tree_any(uint64_t* buf, uint64_t* alt, int m, int K, int32_t* idx_row,
+                                                    float* score_row) {
+  if (m <= 8 * 128) block_topk_tree<2>(buf, alt, m, K, idx_row, score_row);
+  else if (m <= 8 * 256) block_topk_tree<4>(buf, alt, m, K, idx_row, score_row);
+  else block_topk_tree<8>(buf, alt, m, K, idx_row, score_row);
+}
+
 }  // namespace lid
