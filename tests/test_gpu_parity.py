@@ -105,6 +105,40 @@ def test_prefill_split_finish_forms(lid, splits, k_top):
     parity(lid, q, k, w, None, ranges, k_top, "f16", 2, splits, exact=True, label=f"prefill-splits/k{k_top}")
 
 
+@pytest.mark.parametrize("n_above,n_tied", [(400, 3000), (100, 1500), (0, 600), (300, 5000)])
+def test_decode_raw_many_candidates(lid, n_above, n_tied):
+    """Decode over 32768 keys (the raw-score finish) when the k_top-th score
+    is shared by many keys: n_above distinct larger scores, then n_tied keys
+    with one equal score, the rest 0.  The tied keys must be taken in index
+    order; this drives the finish through candidate sets of up to 4096 keys
+    (and, past that, through the tie cut).  Bit exact."""
+    n_kv = 32768
+    rng = np.random.default_rng(n_above + n_tied)
+    q = np.zeros((1, 64, 128), np.float32)
+    q[0, 0, 0] = 1.0
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0] = 1.0
+    k = np.zeros((n_kv, 128), np.float32)
+    k[:, 1:] = rng.integers(-1, 2, (n_kv, 127))       # other dims carry no weight
+    pos = rng.permutation(n_kv)
+    k[pos[:n_above], 0] = np.arange(2, 2 + n_above)   # distinct scores above the tie
+    k[pos[n_above:n_above + n_tied], 0] = 1.0         # the tied score
+    k[pos[n_above + n_tied:], 0] = -rng.integers(0, 3, n_kv - n_above - n_tied)  # ReLU -> 0
+    parity(lid, q.astype(np.float16), k.astype(np.float16), w, None, None, 512, "f16", 3, 0, exact=True,
+           label=f"decode-raw/ties{n_tied}")
+
+
+def test_decode_raw_skewed_threads(lid):
+    """Decode over 32768 keys where half of the finishing threads hold only
+    small scores, so the per-thread bound admits well over 1024 candidates."""
+    n_kv = 32768
+    q, k, w = li.draw_qkw(1, n_kv, 64, 128, "f16", True, seed=4)
+    small = (np.arange(n_kv) % 2048) // 4 >= 256
+    k = k.astype(np.float32)
+    k[small] *= 0.01
+    parity(lid, q, k.astype(np.float16), w, None, None, 512, "f16", 3, 0, label="decode-raw/skewed")
+
+
 @pytest.mark.parametrize("plan,splits", [(2, 0), (2, 1), (2, 4), (3, 0), (3, 3), (1, 0)])
 def test_random_causal_mask_ragged(lid, plan, splits):
     """Random f16 inputs, causal dense mask, ragged n_kv (not a tile multiple)."""
