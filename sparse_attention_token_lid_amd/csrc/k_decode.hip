@@ -64,6 +64,10 @@ constexpr int kRows = kRawMax / BS;   // positions per thread in the raw selecti
 constexpr int kDigitBits = 11;        // radix digit of the raw selection
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kCandMax = 4096;        // candidates gathered into LDS for the exact select
+#ifndef LID_DECODE_DEPTH
+#define LID_DECODE_DEPTH 2
+#endif
+constexpr int kDepth = LID_DECODE_DEPTH;  // key blocks per wave in registers (1 scored + kDepth - 1 loading)
 static_assert(kCandMax == 8 * kTreeCap, "the merge tree takes up to 8 chunks of kTreeCap candidates");
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * D + ((ch ^ (row & 15)) << 3); }
@@ -443,21 +447,27 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     }
   };
 
-  // ping-pong register sets: the loads of one block fly while the other is scored
+  // A ring of kDepth register sets: while a block is scored, the loads of
+  // the next kDepth - 1 blocks of this wave are in flight.
   if (hi > lo) {
-    u32x4 fa[8], fb[8];
-    int64_t b = b0 + wv;
-    uint16_t ma = 0, mb = 0;
-    if (b < b1) { ma = load_mask(b); load_blk(b, fa); }
-    while (b < b1) {
-      const int64_t bn = b + NW;
-      if (bn < b1) { mb = load_mask(bn); load_blk(bn, fb); }
-      score_blk(b, fa, ma);
-      if (bn >= b1) break;
-      const int64_t bnn = bn + NW;
-      if (bnn < b1) { ma = load_mask(bnn); load_blk(bnn, fa); }
-      score_blk(bn, fb, mb);
-      b = bnn;
+    u32x4 f[kDepth][8];
+    uint16_t mk[kDepth];
+    const int64_t bs = b0 + wv;
+#pragma unroll
+    for (int d = 0; d < kDepth - 1; ++d) {
+      const int64_t b = bs + d * NW;
+      mk[d] = 0;
+      if (b < b1) { mk[d] = load_mask(b); load_blk(b, f[d]); }
+    }
+    for (int64_t b = bs; b < b1; b += kDepth * NW) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int64_t bc = b + d * NW;  // scored now, from slot d
+        if (bc >= b1) break;
+        const int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
+        if (bl < b1) { mk[(d + kDepth - 1) % kDepth] = load_mask(bl); load_blk(bl, f[(d + kDepth - 1) % kDepth]); }
+        score_blk(bc, f[d], mk[d]);
+      }
     }
   }
   __syncthreads();
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   if (RAW)
     select_raw(a, t, (int)(nblk * KB), lo, smem);
   else
-    merge_lists(a, ch, t, smem);
+    finish_lists(a, ch, t, smem);
 }
 
 template <int DT, bool RAW>
@@ -525,7 +535,7 @@ size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw) {
     finish = (size_t)NW * kBins * 4 + (size_t)kCandMax * 8 + (size_t)next_pow2(K) * 8 + 2 * BS * 8 +
              sizeof(BlockShared) + (4 * NW + 8) * 4;
   else
-    finish = P > 1 ? merge_lds_need(P, K, ch) : 0;
+    finish = P > 1 ? finish_lds_need(P, K, ch) : 0;
   return scoring > finish ? scoring : finish;
 }
 

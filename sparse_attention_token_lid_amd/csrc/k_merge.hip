@@ -7,12 +7,12 @@ namespace {
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KArgs a, int ch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  merge_lists(a, ch, blockIdx.x, smem);
+  finish_lists(a, ch, blockIdx.x, smem);
 }
 
 }  // namespace
 
-size_t merge_lds_bytes(int P, int K, int ch) { return merge_lds_need(P, K, ch); }
+size_t merge_lds_bytes(int P, int K, int ch) { return finish_lds_need(P, K, ch); }
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st) {
   static bool attr_set = false;

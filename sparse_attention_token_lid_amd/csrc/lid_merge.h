@@ -28,6 +28,101 @@ __host__ __device__ inline size_t merge_lds_need(int P, int K, int ch) {
          2 * sizeof(int) + 2 * (size_t)P + 16 + kSelHistBytes + kSelRedBytes;
 }
 
+// Fast path for next_pow2(K) == kTreeCap and P kTreePrefix <= 4096: the
+// first kTreePrefix entries of every list go through the merge tree
+// (block_topk_tree_any), whose K-th key tau bounds the answer from below.  A
+// list whose last entry read is above tau may hold more of the answer: each
+// such list gives as many further entries as it has given so far, which join
+// the current K best for another tree pass.  Returns false (nothing written)
+// when that would exceed the tree's 4096 candidates; the caller then runs
+// merge_lists.
+constexpr int kTreePrefix = 8;
+__host__ __device__ inline size_t merge_tree_lds_need(int P) {
+  return (size_t)4096 * 8 + (size_t)2048 * 8 + (size_t)kTreeCap * 8 + (size_t)P * 8 + (size_t)P * 16 + 16;
+}
+
+__device__ __forceinline__ bool merge_lists_tree(const KArgs& a, int64_t t, unsigned char* smem) {
+  const int P = a.P, K = a.K;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(smem);    // [4096]
+  uint64_t* alt = cand + 4096;                           // [2048]
+  uint64_t* best = alt + 2048;                           // [kTreeCap] the tree's result
+  uint64_t* last = best + kTreeCap;                      // [P] last entry read per list
+  uint32_t* rd = reinterpret_cast<uint32_t*>(last + P);  // [P] entries read per list
+  uint32_t* fl = rd + P;                                 // [P][3] flagged: list, offset, count
+  int* s_cnt = reinterpret_cast<int*>(fl + 3 * P);       // [0] flagged lists, [1] entries they add
+  const uint64_t* lists = a.lists + (size_t)t * P * K;
+  const int tid = threadIdx.x;
+  // agent-scope loads: the lists may have just been written by other
+  // workgroups of the same launch, on other XCDs
+  auto ld = [&](int lp, int j) -> uint64_t {
+    return __hip_atomic_load(&lists[(size_t)lp * K + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  for (int i = tid; i < P * kTreePrefix; i += kMergeThreads) {
+    const int lp = i / kTreePrefix, j = i % kTreePrefix;
+    const uint64_t key = j < K ? ld(lp, j) : 0ull;
+    cand[i] = key;
+    if (j == kTreePrefix - 1) { last[lp] = key; rd[lp] = kTreePrefix; }
+  }
+  if (tid == 0) { s_cnt[0] = 0; s_cnt[1] = 0; }
+  __syncthreads();
+  int m = P * kTreePrefix;
+  for (;;) {
+    block_topk_tree_any(cand, alt, m, K, nullptr, nullptr, best);
+    const uint64_t tau = best[K - 1];
+    // lists that may hold more keys above tau (keys are unique: a list whose
+    // last entry read is <= tau has nothing further above it)
+    for (int lp = tid; lp < P; lp += kMergeThreads) {
+      const int r = (int)rd[lp];
+      if (r < K && last[lp] > tau) {
+        const int n = r < K - r ? r : K - r;
+        const int f = atomicAdd(&s_cnt[0], 1);
+        fl[3 * f] = (uint32_t)lp;
+        fl[3 * f + 1] = (uint32_t)atomicAdd(&s_cnt[1], n);
+        fl[3 * f + 2] = (uint32_t)n;
+      }
+    }
+    __syncthreads();
+    const int nflag = s_cnt[0], nadd = s_cnt[1];
+    if (nflag == 0) break;
+    if (K + nadd > 4096) return false;
+    for (int f = 0; f < nflag; ++f) {
+      const int lp = (int)fl[3 * f], off = (int)fl[3 * f + 1], n = (int)fl[3 * f + 2], r = (int)rd[lp];
+      for (int j = tid; j < n; j += kMergeThreads) {
+        const uint64_t key = ld(lp, r + j);
+        cand[K + off + j] = key;
+        if (j == n - 1) last[lp] = key;
+      }
+    }
+    for (int i = tid; i < K; i += kMergeThreads) cand[i] = best[i];
+    __syncthreads();  // every rd[] read above precedes its update
+    for (int f = tid; f < nflag; f += kMergeThreads) rd[fl[3 * f]] += fl[3 * f + 2];
+    if (tid == 0) { s_cnt[0] = 0; s_cnt[1] = 0; }
+    m = K + nadd;
+    __syncthreads();
+  }
+  for (int i = tid; i < K; i += kMergeThreads) {
+    a.idx[t * K + i] = key_index(best[i]);
+    if (a.score) a.score[t * K + i] = key_score(best[i]);
+  }
+  return true;
+}
+
+__device__ __forceinline__ void merge_lists(const KArgs& a, int ch, int64_t t, unsigned char* smem);
+
+// LDS for finish_lists(): the larger of the two paths.
+__host__ __device__ inline size_t finish_lds_need(int P, int K, int ch) {
+  const size_t a = merge_lds_need(P, K, ch), b = merge_tree_lds_need(P);
+  return next_pow2(K) == kTreeCap && P * kTreePrefix <= 4096 && b > a ? b : a;
+}
+
+// The final row of query t from its P sorted split lists: the tree fast path
+// when it applies and suffices, else the round-based merge.
+__device__ __forceinline__ void finish_lists(const KArgs& a, int ch, int64_t t, unsigned char* smem) {
+  if (next_pow2(a.K) == kTreeCap && a.P * kTreePrefix <= 4096 && merge_lists_tree(a, t, smem)) return;
+  __syncthreads();
+  merge_lists(a, ch, t, smem);
+}
+
 __device__ __forceinline__ void merge_lists(const KArgs& a, int ch, int64_t t, unsigned char* smem) {
   const int P = a.P, K = a.K;
   const int n2 = next_pow2(K);

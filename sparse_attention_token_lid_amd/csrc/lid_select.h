@@ -176,7 +176,8 @@ __device__ __forceinline__ void block_select_sorted_any(const uint64_t* arr, int
 // straight from LDS, keeping the value of its own block; its block is then
 // bitonic and is sorted by the remaining stages in registers.  buf holds the
 // candidates (8 * 64 E entries, those at or past m read as empty) and alt is
-// LDS for 2048 more; the result goes straight to the output row.
+// LDS for 2048 more; the result goes straight to the output row, or, when
+// out is given, to out[0..kTreeCap) in LDS (visible after the call).
 constexpr int kTreeCap = 512;
 
 template <int EB, int W, int LIN, bool CAPPED>
@@ -219,7 +220,7 @@ __device__ __forceinline__ void wave_merge_block(const uint64_t* A, const uint64
 // output row at the last level.
 template <int E, int LVL>
 __device__ __forceinline__ void tree_level(const uint64_t* src, uint64_t* dst, uint64_t* other, int K,
-                                           int32_t* idx_row, float* score_row) {
+                                           int32_t* idx_row, float* score_row, uint64_t* out) {
   constexpr int CH = kWave * E;
   constexpr int LIN = (CH << (LVL - 1)) < kTreeCap ? (CH << (LVL - 1)) : kTreeCap;
   constexpr int SIN = LVL == 1 ? CH : LIN;
@@ -236,22 +237,25 @@ __device__ __forceinline__ void tree_level(const uint64_t* src, uint64_t* dst, u
 #pragma unroll
     for (int s = 0; s < EB; ++s) {
       const int i = j * kWave * EB + EB * lane + s;
-      if (i < K) {
+      if (out) {
+        out[i] = x[s];
+      } else if (i < K) {
         idx_row[i] = key_index(x[s]);
         if (score_row) score_row[i] = key_score(x[s]);
       }
     }
+    if (out) __syncthreads();
   } else {
 #pragma unroll
     for (int s = 0; s < EB; ++s) dst[g * LOUT + j * kWave * EB + EB * lane + s] = x[s];
     __syncthreads();
-    tree_level<E, LVL + 1>(dst, other, dst, K, idx_row, score_row);
+    tree_level<E, LVL + 1>(dst, other, dst, K, idx_row, score_row, out);
   }
 }
 
 template <int E>
 __device__ __forceinline__ void block_topk_tree(uint64_t* buf, uint64_t* alt, int m, int K, int32_t* idx_row,
-                                                float* score_row) {
+                                                float* score_row, uint64_t* out) {
   static_assert(kSelThreads == 8 * kWave, "eight wavefronts");
   constexpr int CH = kWave * E;
   const int wv = threadIdx.x / kWave, lane = lane_id();
@@ -266,15 +270,15 @@ __device__ __forceinline__ void block_topk_tree(uint64_t* buf, uint64_t* alt, in
 #pragma unroll
   for (int s = 0; s < E; ++s) buf[wv * CH + E * lane + s] = x[s];
   __syncthreads();
-  tree_level<E, 1>(buf, alt, buf, K, idx_row, score_row);
+  tree_level<E, 1>(buf, alt, buf, K, idx_row, score_row, out);
 }
 
 // Dispatch on m (block-uniform): the smallest chunk that holds m / 8.
 __device__ __forceinline__ void block_topk_tree_any(uint64_t* buf, uint64_t* alt, int m, int K, int32_t* idx_row,
-                                                    float* score_row) {
-  if (m <= 8 * 128) block_topk_tree<2>(buf, alt, m, K, idx_row, score_row);
-  else if (m <= 8 * 256) block_topk_tree<4>(buf, alt, m, K, idx_row, score_row);
-  else block_topk_tree<8>(buf, alt, m, K, idx_row, score_row);
+                                                    float* score_row, uint64_t* out = nullptr) {
+  if (m <= 8 * 128) block_topk_tree<2>(buf, alt, m, K, idx_row, score_row, out);
+  else if (m <= 8 * 256) block_topk_tree<4>(buf, alt, m, K, idx_row, score_row, out);
+  else block_topk_tree<8>(buf, alt, m, K, idx_row, score_row, out);
 }
 
 }  // namespace lid

@@ -128,6 +128,24 @@ def test_decode_raw_many_candidates(lid, n_above, n_tied):
            label=f"decode-raw/ties{n_tied}")
 
 
+@pytest.mark.parametrize("start,n_cluster", [(1000, 700), (7000, 5120), (0, 0)])
+def test_decode_lists_clustered(lid, start, n_cluster):
+    """Decode over 65536 keys (split lists, 256 keys per split) when the
+    best keys crowd into a few splits: their lists are read further and
+    further (700 keys over 4 splits), or the candidates outgrow the tree and
+    the round-based merge takes over (5120 keys over 20 splits).  Bit exact."""
+    n_kv = 65536
+    rng = np.random.default_rng(start + n_cluster)
+    q = np.zeros((1, 64, 128), np.float32)
+    q[0, 0, 0] = 1.0
+    w = np.zeros((1, 64), np.float32)
+    w[0, 0] = 1.0
+    k = rng.integers(-1, 2, (n_kv, 128)).astype(np.float32)  # scores 0 or 1 outside the cluster
+    k[start:start + n_cluster, 0] = 2 + rng.permutation(n_cluster) % 2000
+    parity(lid, q.astype(np.float16), k.astype(np.float16), w, None, None, 512, "f16", 3, 0, exact=True,
+           label=f"decode-lists/cluster{n_cluster}")
+
+
 def test_decode_raw_skewed_threads(lid):
     """Decode over 32768 keys where half of the finishing threads hold only
     small scores, so the per-thread bound admits well over 1024 candidates."""
