@@ -146,6 +146,20 @@ def test_decode_lists_clustered(lid, start, n_cluster):
            label=f"decode-lists/cluster{n_cluster}")
 
 
+@pytest.mark.parametrize("n_kv,skew", [(300000, False), (1048576, True)])
+def test_decode_lists_superset(lid, n_kv, skew):
+    """Decode with split lists (a sorted prefix and an unsorted superset of
+    each split's k best).  Ragged splits of ~1172 keys; and splits whose
+    first 512 keys score 100x lower, which makes the per-wave bound admit
+    nearly the whole split, so every split cuts its list by a block select."""
+    q, k, w = li.draw_qkw(1, n_kv, 64, 128, "f16", True, seed=n_kv % 97)
+    if skew:
+        k = k.astype(np.float32)
+        k[(np.arange(n_kv) % 4096) < 512] *= 0.01
+        k = k.astype(np.float16)
+    parity(lid, q, k, w, None, None, 512, "f16", 3, 0, label=f"decode-lists/superset{n_kv}")
+
+
 def test_decode_raw_skewed_threads(lid):
     """Decode over 32768 keys where half of the finishing threads hold only
     small scores, so the per-thread bound admits well over 1024 candidates."""
