@@ -17,12 +17,13 @@
 //  * raw (the query's range fits kRawMax positions): every workgroup writes
 //    its 32-bit ordered scores to the workspace and the last one selects the
 //    k_top best of all of them from registers: a lower bound of the k_top-th
-//    score (from per-thread maxima; 11-bit radix digit passes with
+//    score (from the per-thread top two; 11-bit radix digit passes with
 //    per-wavefront LDS histograms when that bound is too loose) cuts them to
-//    a few thousand candidates, which are selected exactly and sorted in LDS;
-//  * lists: every workgroup selects the k_top best of its split (radix select
-//    + bitonic sort in LDS) and writes them as a sorted list; the last one
-//    merges the P lists (lid_merge.h).
+//    at most a few thousand candidates, which the merge tree of lid_select.h
+//    selects and sorts exactly;
+//  * lists: every workgroup selects the k_top best of its split (register
+//    radix select + bitonic sort) and writes them as a sorted list; the last
+//    one finishes from the P lists (lid_merge.h).
 #include "lid_device.h"
 #include "lid_kernels.h"
 #include "lid_merge.h"
@@ -116,8 +117,9 @@ __device__ __forceinline__ int raw_pos(int r, int tid) { return (r >> 2) * (4 * 
 // key there; position p is key lo + p), sorted, written as the output row.
 // A lower bound of the k_top-th score cuts the n values down to at most
 // kCandMax candidates (v >= thr, which hold the k_top best), which are
-// selected exactly as 64-bit keys (score, index).  The bound comes from the
-// per-thread maxima; when it leaves too many candidates, 11-bit radix digit
+// gathered as 64-bit keys (score, index) and selected exactly (the merge
+// tree when next_pow2(k_top) == 512).  The bound comes from the per-thread
+// top two values; when it leaves too many candidates, 11-bit radix digit
 // passes over the score word with per-wavefront LDS histograms find one.  If
 // a single score value is shared by more than kCandMax positions at the
 // threshold, the tied positions are taken in index order instead.

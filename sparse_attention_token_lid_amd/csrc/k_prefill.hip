@@ -12,7 +12,10 @@
 // per query) and one of P contiguous chunks of the key range those queries can
 // see.  Key tiles of 128 keys x 128 dims (32 KiB) are staged through LDS once
 // per workgroup and shared by its NW wavefronts (double buffered, one barrier
-// per tile).
+// per tile).  With P > 1 each wavefront leaves its split's k_top best in the
+// workspace, and the last workgroup of a query block to finish turns the P
+// lists of each of its queries into the output row (wave_select_lists or
+// wave_merge_lists; with more than 16 splits the merge kernel does it).
 //
 // Per wavefront and 16-key block of a tile: S = Q_t (64 heads x 128) . K^T
 // with v_mfma_f32_16x16x32 (f16 or bf16 in, f32 accumulate): 4 row blocks of

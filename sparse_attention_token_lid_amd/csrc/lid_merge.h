@@ -5,13 +5,16 @@
 //
 // Selection order as in ggml-org llama.cpp issue 25468 ("Root cause"
 // comment): per-token top-k of the masked score; ties by index.  Each list
-// holds the K best keys of one split, sorted descending (empty slots = 0).
-// Lists are read in rounds of ch entries per list: after the first round the
-// workgroup keeps the K best candidates seen so far, and their K-th key tau is
-// a lower bound of the final threshold.  A list whose last entry read is
-// <= tau cannot contribute any more (it is sorted), so it drops out;
-// typically every list drops out after a round or two, and only a small
-// prefix of each list is ever read.
+// holds the K best keys of one split, sorted descending (empty slots = 0),
+// and only a short prefix of most lists can reach the final row.  Two ways:
+//  * merge_lists_tree (next_pow2(K) == 512): the first 8 entries of every
+//    list go through the merge tree of lid_select.h, whose K-th key tau
+//    bounds the answer; lists whose last entry read is above tau give as
+//    many entries again, for another tree pass, until none is left above tau;
+//  * merge_lists: lists are read in rounds of ch entries; after a round the
+//    workgroup keeps the K best candidates seen so far, whose K-th key tau is
+//    a lower bound of the final threshold, and a list whose last entry read
+//    is <= tau drops out (it is sorted).
 #pragma once
 #include "lid_device.h"
 #include "lid_kernels.h"
