@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(DEFAULT_STEPS))
     ap.add_argument("--form", default=None, choices=["none", "mask", "ranges"])
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--mode", default="topk", choices=["topk", "scores"],
+                    help="topk: the fused top-k (the default); scores: the score-only mode (lid_scores), "
+                         "which writes the n_tok x n_kv f32 scores")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -205,15 +208,26 @@ def main():
     sc = torch.empty((wl.n_tok, wl.k_top), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     lib = L.load()
+    scores_mode = args.mode == "scores"
+    if scores_mode:
+        sout = torch.empty((wl.n_tok, wl.n_kv), dtype=torch.float32, device=dev)
+        pshape = L.shape_for(q0, k0, wl.k_top, m0, plan=L.PLAN_PREFILL)
+        plan, splits = "prefill (score-only)", L.plan_of(pshape)[1]
+        ws_bytes = 0
     calls = []
     for (q, k, w, m, r) in sets:
         ptrs = [t.data_ptr() if t is not None else None for t in (q, k, w, m, r)]
-        calls.append((ctypes.byref(shape), *ptrs, idx.data_ptr(), sc.data_ptr(), ws.data_ptr(), ws_bytes, stream))
-    log(f"[bench] plan={plan} splits={splits} workspace={ws_bytes} B copies={copies} "
+        if scores_mode:
+            calls.append((ctypes.byref(shape), *ptrs, sout.data_ptr(), wl.n_kv, stream))
+        else:
+            calls.append((ctypes.byref(shape), *ptrs, idx.data_ptr(), sc.data_ptr(), ws.data_ptr(), ws_bytes,
+                          stream))
+    log(f"[bench] mode={args.mode} plan={plan} splits={splits} workspace={ws_bytes} B copies={copies} "
         f"({per_copy / 2**20:.1f} MiB each) steps={steps} warmup={warmup}")
+    entry = lib.lid_scores if scores_mode else lib.lid_topk
 
     def step(i):
-        rc = lib.lid_topk(*calls[i % copies])
+        rc = entry(*calls[i % copies])
         if rc != 0:
             raise L.LidError(rc)
 
@@ -269,7 +283,7 @@ def main():
         s_cap = torch.cuda.current_stream(dev).cuda_stream
         for i in range(G):
             c = calls[i % copies]
-            rc = lib.lid_topk(*c[:-1], s_cap)
+            rc = entry(*c[:-1], s_cap)
             if rc != 0:
                 raise L.LidError(rc)
     graph.replay()
@@ -289,13 +303,30 @@ def main():
     log(f"[bench] graph: {steps} steps ({steps // G} replays of {G}): {total_ms:.3f} ms GPU "
         f"({(gw1 - gw0) * 1e3:.1f} ms wall), {ms_per_step * 1e3:.2f} us/step")
     # the graph's last replay left the real result in idx / sc: spot-check it is a valid row
-    got = idx[0].cpu().numpy()
-    assert got.max() < wl.n_kv and (got[got >= 0].size == np.unique(got[got >= 0]).size), "invalid top-k row"
+    if scores_mode:
+        assert bool(torch.isfinite(sout[-1]).any()), "no visible score in the last row"
+    else:
+        got = idx[0].cpu().numpy()
+        assert got.max() < wl.n_kv and (got[got >= 0].size == np.unique(got[got >= 0]).size), "invalid top-k row"
     del graph
 
     H, D, K = wl.n_head, wl.head_dim, wl.k_top
     value = pairs * steps / (total_ms * 1e-3)
-    if plan == "decode":
+    if scores_mode:
+        flops = 2.0 * H * D * pairs
+        out_bytes = wl.n_tok * wl.n_kv * 4
+        in_bytes = wl.n_kv * D * 2 + wl.n_tok * (H * D * 2 + H * 4) + (pairs * 2 if form == "mask" else 0)
+        f_mfma = flops / (kern_ms * 1e-3) / PEAK_MFMA_F16
+        f_hbm = (in_bytes + out_bytes) / (kern_ms * 1e-3) / PEAK_HBM_BPS
+        if f_mfma >= f_hbm:
+            roof = {"bound": "mfma", "achieved": flops / (kern_ms * 1e-3) / 1e12, "peak": PEAK_MFMA_F16 / 1e12,
+                    "unit": "TFLOP/s", "frac": f_mfma, "traffic": None, "traffic_unit": "HBM bytes per launch",
+                    "algorithmic_flops": flops, "output_bytes": out_bytes}
+        else:
+            roof = {"bound": "hbm", "achieved": (in_bytes + out_bytes) / (kern_ms * 1e-3) / 1e9,
+                    "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s", "frac": f_hbm, "traffic": None,
+                    "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": in_bytes + out_bytes}
+    elif plan == "decode":
         key_bytes = pairs * D * 2
         alg_bytes = key_bytes + wl.n_tok * (H * D * 2 + H * 4) + (pairs * 2 if form == "mask" else 0) \
             + wl.n_tok * K * 8
@@ -315,7 +346,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}", "n_tok": wl.n_tok, "n_kv": wl.n_kv, "n_head": H,
                    "head_dim": D, "k_top": K, "visible_pairs": pairs, "visibility": form, "plan": plan,
-                   "splits": splits, "workspace_bytes": ws_bytes, "parallelism": "single GPU"},
+                   "splits": splits, "workspace_bytes": ws_bytes, "parallelism": "single GPU", "mode": args.mode},
         "topk_tokens_per_s": wl.n_tok * steps / (total_ms * 1e-3),
         "timing": "HIP-graph replay of the timed steps",
         "eager_ms_per_step": eager_ms_per_step,
@@ -323,7 +354,7 @@ def main():
         "kernel_hash": kernel_source_hash(),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not scores_mode:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(d, form, args.cpu_seconds)
     print(json.dumps(out), flush=True)

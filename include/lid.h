@@ -115,6 +115,26 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
              const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Score-only mode: the output of the pages' fused indexer op itself, without
+ * the top-k.  ggml-org llama.cpp issue 25468, comment "Pinned: master is
+ * missing the fused ggml_lightning_indexer op", gives that op's inputs (q, k,
+ * weights) and its [n_kv, n_tok] score output (ggml order; here row t of a C
+ * [n_tok, n_kv] array); fairydreaming/llama.cpp pull request 2 (last
+ * comment) drops its scale factors and adds the f16 mask.  So
+ *   scores[t * scores_ld + s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:])
+ *                               + mask[t,s]      for s in the query's range,
+ *                               -inf             elsewhere (s < n_kv),
+ * the same v that lid_topk selects from (same kernels, f32 accumulation).
+ *   q, k, w, mask, kv_range  as for lid_topk (k_top, plan and splits of the
+ *                            shape are ignored)
+ *   scores     [n_tok, scores_ld] f32 output, scores_ld >= n_kv; columns
+ *              n_kv .. scores_ld - 1 are not written
+ * This is the n_tok x n_kv buffer that lid_topk never forms: 4 B per pair
+ * (c4-sized: 1 GiB).  No workspace.  Asynchronous on `stream`. */
+int lid_scores(const lid_shape* shape, const void* q, const void* k, const float* w,
+               const uint16_t* mask, const int32_t* kv_range, float* scores, int64_t scores_ld,
+               void* stream);
+
 /* The plan lid_topk would run for `shape` (a lid_plan value), and through
  * `splits_out` (may be NULL) its key splits per query; negative lid_status if
  * the shape is invalid or unsupported. */
@@ -124,9 +144,10 @@ int lid_topk_plan(const lid_shape* shape, int32_t* splits_out);
 const char* lid_status_string(int status);
 
 /* Measurement hook.  With non-NULL hipEvent_t handles, every later lid_topk
- * records `before_scoring` on its stream right before it launches its scoring
- * kernel and `after_scoring` right after, so hipEventElapsedTime gives that
- * kernel's duration; the split merge (if any) falls outside.  NULL, NULL turns
+ * (and lid_scores) records `before_scoring` on its stream right before it
+ * launches its scoring kernel and `after_scoring` right after, so
+ * hipEventElapsedTime gives that kernel's duration; the split merge (if
+ * any) and the score-only mode's fill outside the ranges fall outside.  NULL, NULL turns
  * it off.  Process-wide setting, not synchronised: set it from one thread. */
 void lid_set_profile_events(void* before_scoring, void* after_scoring);
 

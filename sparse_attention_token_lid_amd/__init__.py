@@ -27,8 +27,8 @@ PLAN_AUTO, PLAN_GENERIC, PLAN_PREFILL, PLAN_DECODE = 0, 1, 2, 3
 PLAN_NAMES = {PLAN_GENERIC: "generic", PLAN_PREFILL: "prefill", PLAN_DECODE: "decode"}
 STATUS = {0: "LID_OK", -1: "LID_ERR_INVALID_ARG", -2: "LID_ERR_UNSUPPORTED", -3: "LID_ERR_WORKSPACE",
           -4: "LID_ERR_HIP"}
-EXPORTS = ("lid_topk", "lid_topk_workspace_size", "lid_topk_plan", "lid_status_string", "lid_last_hip_error",
-           "lid_set_profile_events", "lid_version")
+EXPORTS = ("lid_topk", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores", "lid_status_string",
+           "lid_last_hip_error", "lid_set_profile_events", "lid_version")
 
 
 class LidShape(ctypes.Structure):
@@ -67,6 +67,8 @@ def load():
         lib.lid_topk.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lid_topk_workspace_size.restype = ctypes.c_size_t
         lib.lid_topk_workspace_size.argtypes = [ctypes.POINTER(LidShape)]
+        lib.lid_scores.restype = ctypes.c_int
+        lib.lid_scores.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         lib.lid_topk_plan.restype = ctypes.c_int
         lib.lid_topk_plan.argtypes = [ctypes.POINTER(LidShape), ctypes.POINTER(ctypes.c_int32)]
         lib.lid_status_string.restype = ctypes.c_char_p
@@ -152,6 +154,43 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
     if rc != 0:
         raise LidError(rc)
     return idx, score
+
+
+def scores(q, k, w, mask=None, kv_range=None, *, out=None, stream=None):
+    """Score-only mode: the [n_tok, n_kv] f32 masked scores (-inf outside each
+    query's range), the output of the fused indexer op without the top-k.
+    `out` may be an f32 [n_tok, ld] tensor with ld >= n_kv."""
+    import torch
+    if q.dim() != 3 or k.dim() != 2 or w.dim() != 2:
+        raise ValueError("q [n_tok,H,D], k [n_kv,D], w [n_tok,H] expected")
+    n_tok, H, D = q.shape
+    n_kv = k.shape[0]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("lid.scores runs on the GPU only (q is on %s)" % dev)
+    for name, t in (("q", q), ("k", k), ("w", w), ("mask", mask), ("kv_range", kv_range)):
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if k.dtype != q.dtype or k.shape[1] != D or w.shape != (n_tok, H) or w.dtype != torch.float32:
+        raise ValueError("dtype/shape mismatch among q, k, w")
+    if mask is not None:
+        if mask.dtype not in (torch.float16, torch.int16, torch.uint16) or mask.dim() != 2 or mask.shape[0] != n_tok:
+            raise ValueError("mask must be float16 [n_tok, mask_ld]")
+    if kv_range is not None and (kv_range.dtype != torch.int32 or tuple(kv_range.shape) != (n_tok, 2)):
+        raise ValueError("kv_range must be int32 [n_tok, 2]")
+    if out is None:
+        out = torch.empty((n_tok, n_kv), dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.shape[0] != n_tok or out.stride(1) != 1 \
+            or out.stride(0) < n_kv:
+        raise ValueError("out must be float32 [n_tok, >= n_kv] with unit column stride")
+    shape = shape_for(q, k, 1, mask)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = load().lid_scores(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(mask), _ptr(kv_range), _ptr(out),
+                           out.stride(0), stream)
+    if rc != 0:
+        raise LidError(rc)
+    return out[:, :n_kv]
 
 
 def set_profile_events(before, after):

@@ -174,7 +174,11 @@ __device__ __forceinline__ void wave_select_lists(const KArgs& a, int64_t t, Wav
   wave_write_row(st.buf, a.K, a.idx + t * a.K, a.score ? a.score + t * a.K : nullptr, nullptr);
 }
 
-template <int NW, int DT, bool MK>
+// SC: score-only mode.  Every (query, key) score of the workgroup's chunk
+// is written to a.scores (f32, row stride a.scores_ld; -inf outside the
+// query's range or under a -inf mask) instead of entering a top-k: the output
+// of the pages' fused op, from the same tiles, MFMAs and epilogue.
+template <int NW, int DT, bool MK, bool SC>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   using M = Mfma<DT>;
   using T = typename M::T;
@@ -400,6 +404,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       const uint64_t inr = u.live ? (below_hi & ~below_lo) : 0ull;
       z.v = lane_select(inr, z.v, -__builtin_inff());
       asm volatile("" : "+v"(z.v));
+    } else if (i == 7 && SC) {
+      // 64 consecutive keys per store: 256 contiguous bytes of the row
+      const int s = u.s0 + lane;
+      if (u.live && has_q && s < n_kv) __builtin_nontemporal_store(z.v, a.scores + t * a.scores_ld + s);
     } else if (i == 7) {
       const bool pass = z.v >= st.tau_v;
       const uint64_t m = ballot(pass);
@@ -419,6 +427,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // Make room for one more unit: compaction to the k_top best when fewer than
   // 128 free slots remain (rare once the stream is long).
   auto room = [&]() {
+    if (SC) return;
     st.count = __builtin_amdgcn_readfirstlane(st.count);  // keep it scalar (see uniform_u64)
     if (st.count > st.cap - 2 * kWave) wave_topk_trim(st);
   };
@@ -430,9 +439,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // The flags are double buffered by tile parity: a wave can only rewrite a
   // slot after the next barrier, which every reader of it has passed.
   auto flag_need = [&](int it) {
+    if (SC) return;
     if (lane == 0) cflag[(it & 1) * NW + wv] = st.count > st.cap - 3 * kWave ? 1u : 0u;
   };
   auto sync_compact = [&](int it) {
+    if (SC) return;
     uint32_t any = 0;
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) any |= cflag[(it & 1) * NW + w2];
@@ -539,6 +550,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     for (int i = 0; i < 8; ++i) insert_slice(u1, i, z);
   }
 
+  if (SC) return;  // score-only mode: nothing to finish
+
   if (has_q && a.fuse == 2) {
     // unsorted split list: the K best (all present keys if fewer), 0-padded
     wave_topk_reduce(st);
@@ -583,19 +596,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   }
 }
 
-template <int NW, int DT, bool MK>
+template <int NW, int DT, bool MK, bool SC = false>
 hipError_t launch_one(const KArgs& a, hipStream_t st) {
   const size_t lds = prefill_lds_bytes(NW, a.cap);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NW, DT, MK>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NW, DT, MK, SC>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 2 * kTileBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t nqb = (a.n_tok + NW - 1) / NW;
   dim3 grid((unsigned)(nqb * a.P));
-  hipLaunchKernelGGL((prefill_kernel<NW, DT, MK>), grid, dim3(NW * 64), lds, st, a);
+  hipLaunchKernelGGL((prefill_kernel<NW, DT, MK, SC>), grid, dim3(NW * 64), lds, st, a);
   return hipGetLastError();
 }
 
@@ -614,6 +627,12 @@ hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {
   }
   if (nw == 8) return mk ? launch_one<8, 2, true>(a, st) : launch_one<8, 2, false>(a, st);
   return mk ? launch_one<4, 2, true>(a, st) : launch_one<4, 2, false>(a, st);
+}
+
+hipError_t launch_prefill_scores(const KArgs& a, hipStream_t st) {
+  const bool mk = a.mask != nullptr;
+  if (a.dtype == 1) return mk ? launch_one<8, 1, true, true>(a, st) : launch_one<8, 1, false, true>(a, st);
+  return mk ? launch_one<8, 2, true, true>(a, st) : launch_one<8, 2, false, true>(a, st);
 }
 
 }  // namespace lid

@@ -93,7 +93,7 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (!P) {
       // enough (query block, split) workgroups for one per CU, but never a
       // split shorter than 2048 keys
-      const int64_t nqb = cdiv(s->n_tok, pl->nw);
+      const int64_t nqb = s->n_tok > 0 ? cdiv(s->n_tok, pl->nw) : 1;
       int64_t want = cdiv(kCUs, nqb);
       const int64_t min_tiles = 2048 / kPrefillTile;
       const int64_t cap = tiles / min_tiles > 1 ? tiles / min_tiles : 1;
@@ -230,6 +230,56 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
     e = launch_merge(a, pl.ch, st);
     if (e != hipSuccess) return hip_fail(e);
   }
+  return LID_OK;
+}
+
+int lid_scores(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
+               const int32_t* kv_range, float* scores, int64_t scores_ld, void* stream) {
+  if (!shape) return LID_ERR_INVALID_ARG;
+  // the scoring plan: the prefill kernel's key splits (k_top does not matter)
+  lid_shape ps = *shape;
+  ps.k_top = 512;
+  ps.plan = LID_PLAN_AUTO;
+  ps.splits = 0;
+  const bool mfma = (ps.qk_dtype == LID_F16 || ps.qk_dtype == LID_BF16) && ps.n_head == kMfmaHeads &&
+                    ps.head_dim == kMfmaDim && shape->plan != LID_PLAN_GENERIC;
+  ps.plan = mfma ? LID_PLAN_PREFILL : LID_PLAN_GENERIC;
+  Plan pl;
+  int rc = make_plan(&ps, &pl);
+  if (rc != LID_OK) return rc;
+  const lid_shape& s = *shape;
+  if (s.n_tok == 0 || s.n_kv == 0) return LID_OK;
+  if (!q || !k || !w || !scores || scores_ld < s.n_kv) return LID_ERR_INVALID_ARG;
+  if (mask && s.mask_ld < s.n_kv) return LID_ERR_INVALID_ARG;
+  if (mfma && ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k) & 15)))
+    return LID_ERR_INVALID_ARG;
+  if (!mfma && s.n_tok * cdiv(s.n_kv, 256) > INT32_MAX) return LID_ERR_UNSUPPORTED;
+
+  KArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.w = w;
+  a.mask = mask;
+  a.kv_range = kv_range;
+  a.scores = scores;
+  a.scores_ld = scores_ld;
+  a.n_tok = s.n_tok;
+  a.n_kv = s.n_kv;
+  a.mask_ld = mask ? s.mask_ld : 0;
+  a.H = s.n_head;
+  a.D = s.head_dim;
+  a.K = ps.k_top;
+  a.P = pl.P;
+  a.cap = pl.cap;
+  a.dtype = s.qk_dtype;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (mfma && kv_range && (e = launch_scores_fill(a, st)) != hipSuccess) return hip_fail(e);
+  if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
+  e = mfma ? launch_prefill_scores(a, st) : launch_generic_scores(a, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
   return LID_OK;
 }
 

@@ -17,6 +17,8 @@ struct KArgs {
   float* score;             // [n_tok, K], or null
   uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1)
   uint32_t* raw;            // decode, raw form: [n_tok, raw_ld] ordered scores (0 = no key)
+  float* scores;            // score-only mode: [n_tok, scores_ld] f32 output
+  int64_t scores_ld;
   uint32_t* counters;       // finished-workgroup counters (zero between launches): decode [n_tok],
                             // prefill with a fused finish [query blocks]
   int64_t n_tok, n_kv, mask_ld, raw_ld;
@@ -39,6 +41,9 @@ constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);
+hipError_t launch_prefill_scores(const KArgs& a, hipStream_t st);  // score-only mode, 8 queries per workgroup
+hipError_t launch_scores_fill(const KArgs& a, hipStream_t st);     // -inf outside each query's range
+hipError_t launch_generic_scores(const KArgs& a, hipStream_t st);  // score-only mode, any shape
 size_t prefill_lds_bytes(int nw, int cap);
 
 hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, bool raw, hipStream_t st);

@@ -120,3 +120,20 @@ def test_status_strings_and_version(L):
 
 def test_workspace_size_invalid_is_zero(L):
     assert L.workspace_size(shape_of("c3", k_top=0)) == 0
+
+
+def test_scores_errors_before_launch(L):
+    """lid_scores rejects bad arguments before any launch (fake addresses)."""
+    lib = L.load()
+    ok = shape_of("c3")
+
+    def sc(shape, q=16, k=16, w=16, mask=None, rng=None, out=16, ld=None):
+        return lib.lid_scores(ctypes.byref(shape), q, k, w, mask, rng, out, shape.n_kv if ld is None else ld, None)
+
+    assert sc(shape_of("c3", qk_dtype=7)) == -1               # bad dtype
+    assert sc(ok, out=None) == -1                              # no output
+    assert sc(ok, ld=ok.n_kv - 1) == -1                        # row stride below n_kv
+    assert sc(ok, q=None) == -1
+    assert sc(ok, q=8) == -1                                   # MFMA path needs 16-byte aligned q, k
+    assert sc(shape_of("c3", mask_ld=5), mask=16) == -1        # mask stride below n_kv
+    assert sc(shape_of("c3", n_tok=0)) == 0                    # nothing to do
