@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lid_oracle.c")
 _LIB = os.path.join(_HERE, "liblid_oracle.so")
 
-DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2, "f8e4m3": 3}
 _lib = None
 
 
@@ -53,6 +53,13 @@ def load_library(path: str):
                                     vp, vp, vp, i32]
     lib.lid_oracle_scores.restype = ctypes.c_int
     lib.lid_oracle_scores.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, i32]
+    lib.lid_oracle_topk_scaled.restype = ctypes.c_int
+    lib.lid_oracle_topk_scaled.argtypes = [i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp,
+                                           vp, vp, vp, i32]
+    lib.lid_oracle_scores_scaled.restype = ctypes.c_int
+    lib.lid_oracle_scores_scaled.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, i32]
+    lib.lid_oracle_f8e4m3_to_f64.restype = ctypes.c_double
+    lib.lid_oracle_f8e4m3_to_f64.argtypes = [ctypes.c_uint8]
     lib.lid_oracle_f16_to_f64.restype = ctypes.c_double
     lib.lid_oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
     lib.lid_oracle_bf16_to_f64.restype = ctypes.c_double
@@ -88,6 +95,9 @@ class Oracle:
     def bf16_to_f64(self, bits):
         return self._lib.lid_oracle_bf16_to_f64(bits)
 
+    def f8e4m3_to_f64(self, bits):
+        return self._lib.lid_oracle_f8e4m3_to_f64(bits)
+
 
 def _dtype_of(x: np.ndarray, qk_dtype: str | None) -> str:
     if qk_dtype is not None:
@@ -96,7 +106,7 @@ def _dtype_of(x: np.ndarray, qk_dtype: str | None) -> str:
         return "f32"
     if x.dtype == np.float16:
         return "f16"
-    raise ValueError("pass qk_dtype='bf16' for uint16 bf16 bit patterns")
+    raise ValueError("pass qk_dtype='bf16' for uint16 bf16 bit patterns, 'f8e4m3' for uint8 E4M3 bytes")
 
 
 def _ptr(a):
@@ -120,11 +130,25 @@ def _prep(q, k, w, mask, kv_range, qk_dtype, rows):
     return q, k, w, mask, kv_range, dt
 
 
+def _scales(q_scale, k_scale, rows):
+    if q_scale is None and k_scale is None:
+        return None, None
+    if q_scale is None or k_scale is None:
+        raise ValueError("q_scale and k_scale go together")
+    q_scale = np.asarray(q_scale, dtype=np.float32)
+    if rows is not None:
+        q_scale = q_scale[np.asarray(rows, dtype=np.int64)]
+    return np.ascontiguousarray(q_scale), np.ascontiguousarray(k_scale, dtype=np.float32)
+
+
 def topk(q, k, w, mask=None, kv_range=None, k_top=512, qk_dtype=None, rows=None, threads=0,
-         _lib=None):
+         q_scale=None, k_scale=None, _lib=None):
     """Oracle top-k.  Returns (idx int32 [n,k_top], score f32 [n,k_top], maxabs).
 
-    rows: optional query subset (the oracle then runs only those rows)."""
+    rows: optional query subset (the oracle then runs only those rows).
+    q_scale [n_tok, H], k_scale [n_kv] (f32): per-row scales of q and k
+    (the FP8 convention; both or neither)."""
+    qs, ks = _scales(q_scale, k_scale, rows)
     q, k, w, mask, kv_range, dt = _prep(q, k, w, mask, kv_range, qk_dtype, rows)
     n_tok, H, D = q.shape
     n_kv = k.shape[0]
@@ -133,24 +157,35 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, qk_dtype=None, rows=None,
     maxabs = ctypes.c_double(0.0)
     mask_ld = 0 if mask is None else mask.shape[1]
     lib = _lib or _load()
-    rc = lib.lid_oracle_topk(n_tok, n_kv, H, D, k_top, DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(w),
-                             _ptr(mask), mask_ld, _ptr(kv_range), _ptr(idx), _ptr(score),
-                             ctypes.addressof(maxabs), threads)
+    if qs is not None:
+        rc = lib.lid_oracle_topk_scaled(n_tok, n_kv, H, D, k_top, DTYPE_CODE[dt], _ptr(q), _ptr(qs), _ptr(k),
+                                        _ptr(ks), _ptr(w), _ptr(mask), mask_ld, _ptr(kv_range), _ptr(idx),
+                                        _ptr(score), ctypes.addressof(maxabs), threads)
+    else:
+        rc = lib.lid_oracle_topk(n_tok, n_kv, H, D, k_top, DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(w),
+                                 _ptr(mask), mask_ld, _ptr(kv_range), _ptr(idx), _ptr(score),
+                                 ctypes.addressof(maxabs), threads)
     if rc != 0:
         raise RuntimeError(f"lid_oracle_topk failed: {rc}")
     return idx, score, maxabs.value
 
 
-def scores(q, k, w, mask=None, kv_range=None, qk_dtype=None, rows=None, threads=0, _lib=None):
+def scores(q, k, w, mask=None, kv_range=None, qk_dtype=None, rows=None, threads=0, q_scale=None, k_scale=None,
+           _lib=None):
     """Full masked f32 score matrix [n, n_kv] (-inf where not visible)."""
+    qs, ks = _scales(q_scale, k_scale, rows)
     q, k, w, mask, kv_range, dt = _prep(q, k, w, mask, kv_range, qk_dtype, rows)
     n_tok, H, D = q.shape
     n_kv = k.shape[0]
     v = np.empty((n_tok, n_kv), dtype=np.float32)
     mask_ld = 0 if mask is None else mask.shape[1]
     lib = _lib or _load()
-    rc = lib.lid_oracle_scores(n_tok, n_kv, H, D, DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(w),
-                               _ptr(mask), mask_ld, _ptr(kv_range), _ptr(v), threads)
+    if qs is not None:
+        rc = lib.lid_oracle_scores_scaled(n_tok, n_kv, H, D, DTYPE_CODE[dt], _ptr(q), _ptr(qs), _ptr(k), _ptr(ks),
+                                          _ptr(w), _ptr(mask), mask_ld, _ptr(kv_range), _ptr(v), threads)
+    else:
+        rc = lib.lid_oracle_scores(n_tok, n_kv, H, D, DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(w),
+                                   _ptr(mask), mask_ld, _ptr(kv_range), _ptr(v), threads)
     if rc != 0:
         raise RuntimeError(f"lid_oracle_scores failed: {rc}")
     return v
@@ -162,3 +197,7 @@ def f16_to_f64(bits: int) -> float:
 
 def bf16_to_f64(bits: int) -> float:
     return _load().lid_oracle_bf16_to_f64(bits)
+
+
+def f8e4m3_to_f64(bits: int) -> float:
+    return _load().lid_oracle_f8e4m3_to_f64(bits)

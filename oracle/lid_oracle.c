@@ -25,6 +25,16 @@
  *     [512 x n_tok] int32, 1 MiB, same comment), ordered by score descending
  *     and, among equal f32 scores, by key index ascending.
  *
+ * FP8 inputs (lid_oracle_topk_scaled / lid_oracle_scores_scaled).  The pages'
+ * DeepSeek-V4 path quantises the indexer to FP4 after a Hadamard rotation
+ * (ggml-org llama.cpp PR 22378, the batched-prefill commit) and its KV cache
+ * to FP8 E4M3 (the DSV4 CUDA-kernel plan, section "dsv4_fp8_kv_quantize"),
+ * but gives no scale convention for the indexer, so a synthetic one is used:
+ * q and k are OCP FP8 E4M3 bytes with a positive f32 scale per
+ * query head row and per key row, q[t,h,:] = e4m3(q8[t,h,:]) * q_scale[t,h],
+ * k[s,:] = e4m3(k8[s,:]) * k_scale[s]; these dequantised values (exact in
+ * double) then go through steps 1-4 unchanged.
+ *
  * Readings where the pages are silent: -0 scores are treated as +0; fewer
  * than k_top visible keys pad the row with index -1 / score -inf; an optional
  * per-query half-open key range [lo, hi) restricts the keys scored (keys
@@ -38,7 +48,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_F8E4M3 = 3 };
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENONFINITE = -2, ORC_ENOMEM = -3 };
 
 /* IEEE binary16 -> double, written from the format definition:
@@ -67,11 +77,30 @@ double lid_oracle_bf16_to_f64(uint16_t b)
     return (double)f;
 }
 
+/* OCP FP8 E4M3 (E4M3FN) -> double, written from the format definition:
+ * 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits; exponent field 0 is
+ * subnormal (m * 2^-9); no infinities; S.1111.111 is NaN. */
+double lid_oracle_f8e4m3_to_f64(uint8_t x)
+{
+    int sign = (x >> 7) & 1;
+    int e = (x >> 3) & 0xF;
+    int m = x & 0x7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -9);                  /* subnormal: (m/8) * 2^-6 */
+    else if (e == 15 && m == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + m), e - 10);        /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
 static double decode(const void* p, int dtype, int64_t i)
 {
     switch (dtype) {
     case ORC_F32: return (double)((const float*)p)[i];
     case ORC_F16: return lid_oracle_f16_to_f64(((const uint16_t*)p)[i]);
+    case ORC_F8E4M3: return lid_oracle_f8e4m3_to_f64(((const uint8_t*)p)[i]);
     default:      return lid_oracle_bf16_to_f64(((const uint16_t*)p)[i]);
     }
 }
@@ -139,7 +168,7 @@ static int check_args(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t
 {
     if (n_tok < 0 || n_kv < 0 || n_kv > INT32_MAX || H <= 0 || D <= 0)
         return ORC_EINVAL;
-    if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16)
+    if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16 && dtype != ORC_F8E4M3)
         return ORC_EINVAL;
     if ((n_tok > 0 && (!q || !w)) || (n_kv > 0 && !k))
         return ORC_EINVAL;
@@ -148,12 +177,16 @@ static int check_args(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t
     return ORC_OK;
 }
 
-static double* decode_keys(const void* k, int dtype, int64_t n_kv, int D)
+/* Decoded key rows, each times its scale when k_scale is given. */
+static double* decode_keys(const void* k, int dtype, int64_t n_kv, int D, const float* k_scale)
 {
     double* kd = (double*)malloc(sizeof(double) * (size_t)(n_kv > 0 ? n_kv : 1) * (size_t)D);
     if (!kd) return NULL;
-    for (int64_t i = 0; i < n_kv * D; ++i)
+    for (int64_t i = 0; i < n_kv * D; ++i) {
         kd[i] = decode(k, dtype, i);
+        if (k_scale)
+            kd[i] *= (double)k_scale[i / D];
+    }
     return kd;
 }
 
@@ -168,16 +201,17 @@ static double* decode_keys(const void* k, int dtype, int64_t n_kv, int D)
  *   maxabs_out: max |I[t,s]| over every visible pair (may be NULL)
  *   n_threads: OpenMP threads (<= 0: runtime default)
  */
-int lid_oracle_topk(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k_top,
-                    int32_t dtype, const void* q, const void* k, const float* w,
-                    const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
-                    int32_t* idx_out, float* score_out, double* maxabs_out, int32_t n_threads)
+static int topk_impl(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k_top,
+                     int32_t dtype, const void* q, const void* k, const float* w,
+                     const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
+                     int32_t* idx_out, float* score_out, double* maxabs_out, int32_t n_threads,
+                     const float* q_scale, const float* k_scale)
 {
     int rc = check_args(n_tok, n_kv, H, D, dtype, q, k, w, mask_ld, mask);
     if (rc) return rc;
     if (k_top <= 0 || !idx_out) return ORC_EINVAL;
 
-    double* kd = decode_keys(k, dtype, n_kv, D);
+    double* kd = decode_keys(k, dtype, n_kv, D, k_scale);
     if (!kd) return ORC_ENOMEM;
 
     double maxabs = 0.0;
@@ -199,8 +233,11 @@ int lid_oracle_topk(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k
             free(qd); free(wd); free(c);
             continue;
         }
-        for (int64_t i = 0; i < (int64_t)H * D; ++i)
+        for (int64_t i = 0; i < (int64_t)H * D; ++i) {
             qd[i] = decode(q, dtype, t * H * D + i);
+            if (q_scale)
+                qd[i] *= (double)q_scale[t * H + i / D];
+        }
         for (int h = 0; h < H; ++h)
             wd[h] = (double)w[t * H + h];
 
@@ -230,21 +267,42 @@ int lid_oracle_topk(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k
     return err;
 }
 
+int lid_oracle_topk(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k_top,
+                    int32_t dtype, const void* q, const void* k, const float* w,
+                    const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
+                    int32_t* idx_out, float* score_out, double* maxabs_out, int32_t n_threads)
+{
+    return topk_impl(n_tok, n_kv, H, D, k_top, dtype, q, k, w, mask, mask_ld, kv_range, idx_out,
+                     score_out, maxabs_out, n_threads, NULL, NULL);
+}
+
+/* The same with per-row scales on q ([n_tok, H] f32) and k ([n_kv] f32). */
+int lid_oracle_topk_scaled(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k_top,
+                           int32_t dtype, const void* q, const float* q_scale, const void* k,
+                           const float* k_scale, const float* w, const uint16_t* mask,
+                           int64_t mask_ld, const int32_t* kv_range, int32_t* idx_out,
+                           float* score_out, double* maxabs_out, int32_t n_threads)
+{
+    if (!q_scale || !k_scale) return ORC_EINVAL;
+    return topk_impl(n_tok, n_kv, H, D, k_top, dtype, q, k, w, mask, mask_ld, kv_range, idx_out,
+                     score_out, maxabs_out, n_threads, q_scale, k_scale);
+}
+
 /*
  * The full masked score matrix v[t,s] (f32, -inf where not visible) -- the
  * output of the pages' un-selected fused op (issue 25468, comment "Pinned:
  * master is missing the fused ggml_lightning_indexer op": output shape
  * [n_kv, n_tok] in ggml order).  For small problems only: it is n_tok x n_kv.
  */
-int lid_oracle_scores(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t dtype,
-                      const void* q, const void* k, const float* w,
-                      const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
-                      float* v_out, int32_t n_threads)
+static int scores_impl(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t dtype,
+                       const void* q, const void* k, const float* w,
+                       const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
+                       float* v_out, int32_t n_threads, const float* q_scale, const float* k_scale)
 {
     int rc = check_args(n_tok, n_kv, H, D, dtype, q, k, w, mask_ld, mask);
     if (rc) return rc;
     if (!v_out) return ORC_EINVAL;
-    double* kd = decode_keys(k, dtype, n_kv, D);
+    double* kd = decode_keys(k, dtype, n_kv, D, k_scale);
     if (!kd) return ORC_ENOMEM;
     int err = 0;
 #ifdef _OPENMP
@@ -257,8 +315,11 @@ int lid_oracle_scores(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t
         double* qd = (double*)malloc(sizeof(double) * (size_t)H * (size_t)D);
         double* wd = (double*)malloc(sizeof(double) * (size_t)H);
         if (!qd || !wd) { err = ORC_ENOMEM; free(qd); free(wd); continue; }
-        for (int64_t i = 0; i < (int64_t)H * D; ++i)
+        for (int64_t i = 0; i < (int64_t)H * D; ++i) {
             qd[i] = decode(q, dtype, t * H * D + i);
+            if (q_scale)
+                qd[i] *= (double)q_scale[t * H + i / D];
+        }
         for (int h = 0; h < H; ++h)
             wd[h] = (double)w[t * H + h];
         int64_t lo, hi;
@@ -275,4 +336,24 @@ int lid_oracle_scores(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t
     }
     free(kd);
     return err;
+}
+
+int lid_oracle_scores(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t dtype,
+                      const void* q, const void* k, const float* w,
+                      const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
+                      float* v_out, int32_t n_threads)
+{
+    return scores_impl(n_tok, n_kv, H, D, dtype, q, k, w, mask, mask_ld, kv_range, v_out, n_threads,
+                       NULL, NULL);
+}
+
+int lid_oracle_scores_scaled(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t dtype,
+                             const void* q, const float* q_scale, const void* k,
+                             const float* k_scale, const float* w, const uint16_t* mask,
+                             int64_t mask_ld, const int32_t* kv_range, float* v_out,
+                             int32_t n_threads)
+{
+    if (!q_scale || !k_scale) return ORC_EINVAL;
+    return scores_impl(n_tok, n_kv, H, D, dtype, q, k, w, mask, mask_ld, kv_range, v_out, n_threads,
+                       q_scale, k_scale);
 }

@@ -100,6 +100,74 @@ def test_bf16_decode_exhaustive(oracle_lib):
             assert got == ref[b], hex(b)
 
 
+def test_f8e4m3_decode_exhaustive(oracle_lib):
+    """All 256 OCP FP8 E4M3 patterns against torch's float8_e4m3fn decode."""
+    torch = pytest.importorskip("torch")
+    bits = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = bits.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        got = oracle_lib.f8e4m3_to_f64(b)
+        if np.isnan(ref[b]):
+            assert math.isnan(got), hex(b)
+        else:
+            assert got == ref[b] and math.copysign(1, got) == math.copysign(1, ref[b]), hex(b)
+
+
+def _f8_bytes(rng, shape):
+    """Random E4M3 bytes without the NaN patterns and with moderate exponents."""
+    b = rng.integers(0, 256, shape).astype(np.uint8)
+    e = (b >> 3) & 15
+    b = np.where(e > 11, b & 0xC7 | (11 << 3), b).astype(np.uint8)   # exponent <= 11 (|x| < 32)
+    return b
+
+
+def _f8_to_f32(b):
+    """E4M3 bytes -> exact f32 values, from the format definition (independent of the oracle)."""
+    b = b.astype(np.int64)
+    s, e, m = b >> 7, (b >> 3) & 15, b & 7
+    v = np.where(e == 0, m * 2.0 ** -9, (8 + m) * 2.0 ** (e - 10))
+    return np.where(s == 1, -v, v).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_f8_scaled_equals_dequantised(oracle_lib, seed):
+    """FP8 q/k with per-row power-of-two scales give exactly the result of
+    the dequantised f32 inputs (every value is exact in f32), for non-uniform
+    scales per query head row and per key row."""
+    rng = np.random.default_rng(40 + seed)
+    n_tok, n_kv, H, D = 3, 200, 4, 32
+    q8, k8 = _f8_bytes(rng, (n_tok, H, D)), _f8_bytes(rng, (n_kv, D))
+    qs = (2.0 ** rng.integers(-3, 4, (n_tok, H))).astype(np.float32)
+    ks = (2.0 ** rng.integers(-3, 4, n_kv)).astype(np.float32)
+    w = rng.random((n_tok, H)).astype(np.float32)
+    qf = _f8_to_f32(q8) * qs[:, :, None]
+    kf = _f8_to_f32(k8) * ks[:, None]
+    a = oracle_lib.topk(q8, k8, w, k_top=50, qk_dtype="f8e4m3", q_scale=qs, k_scale=ks)
+    b = oracle_lib.topk(qf, kf, w, k_top=50)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    va = oracle_lib.scores(q8, k8, w, qk_dtype="f8e4m3", q_scale=qs, k_scale=ks)
+    vb = oracle_lib.scores(qf, kf, w)
+    assert np.array_equal(va, vb)
+
+
+def test_f8_closed_form_single_head_single_dim(oracle_lib):
+    """H=1, D=1, w=1 with FP8 q, k and scales: I[s] = max(0, q qs k[s] ks[s]),
+    computed here in numpy f64 from the format definition; a plain stable sort."""
+    rng = np.random.default_rng(77)
+    n_kv, k_top = 300, 40
+    q8, k8 = _f8_bytes(rng, (2, 1, 1)), _f8_bytes(rng, (n_kv, 1))
+    qs = rng.uniform(0.5, 2.0, (2, 1)).astype(np.float32)
+    ks = rng.uniform(0.5, 2.0, n_kv).astype(np.float32)
+    w = np.ones((2, 1), np.float32)
+    idx, sc, _ = oracle_lib.topk(q8, k8, w, k_top=k_top, qk_dtype="f8e4m3", q_scale=qs, k_scale=ks)
+    qv, kv = _f8_to_f32(q8).astype(np.float64), _f8_to_f32(k8).astype(np.float64)
+    for t in range(2):
+        v = np.maximum(0.0, (qv[t, 0, 0] * qs[t, 0]) * (kv[:, 0] * ks.astype(np.float64))).astype(np.float32)
+        order = np.argsort(-v, kind="stable")[:k_top]
+        assert idx[t].tolist() == order.tolist()
+        assert np.array_equal(sc[t], v[order])
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_closed_form_single_head_single_dim(oracle_lib, seed):
     """H=1, D=1, w=1: I[s] = max(0, q*k[s]); the top-k is a plain stable sort."""

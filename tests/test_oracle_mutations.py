@@ -32,6 +32,11 @@ MUTATIONS = {
     "f16_subnormal": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -23);"),
     "no_padding": ("idx_out[t * k_top + j] = valid ? (int32_t)c[j].s : -1;", "idx_out[t * k_top + j] = valid ? (int32_t)c[j].s : 0;"),
     "neg_zero_kept": ("*out = v + 0.0f;", "*out = v;"),
+    "f8_exponent_bias": ("v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);"),
+    "f8_subnormal": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "k_scale_wrong_row": ("kd[i] *= (double)k_scale[i / D];", "kd[i] *= (double)k_scale[i % D];"),
+    "q_scale_wrong_head": ("qd[i] *= (double)q_scale[t * H + i / D];\n        }\n        for (int h = 0; h < H; ++h)\n            wd[h] = (double)w[t * H + h];\n\n        int64_t n = 0;",
+                           "qd[i] *= (double)q_scale[t * H];\n        }\n        for (int h = 0; h < H; ++h)\n            wd[h] = (double)w[t * H + h];\n\n        int64_t n = 0;"),
 }
 
 PINS = [
@@ -43,6 +48,9 @@ PINS = [
     lambda o: T.test_bruteforce_random(o, "f16"),
     T.test_f16_decode_exhaustive,
     T.test_invariants_random,
+    T.test_f8e4m3_decode_exhaustive,
+    lambda o: T.test_f8_scaled_equals_dequantised(o, 0),
+    T.test_f8_closed_form_single_head_single_dim,
 ]
 
 
