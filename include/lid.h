@@ -60,7 +60,7 @@ extern "C" {
 #endif
 
 /* dtype of q and k.  w is always f32, mask always f16 (IEEE binary16 bits). */
-typedef enum { LID_F32 = 0, LID_F16 = 1, LID_BF16 = 2 } lid_dtype;
+typedef enum { LID_F32 = 0, LID_F16 = 1, LID_BF16 = 2, LID_F8E4M3 = 3 } lid_dtype;
 
 typedef enum {
     LID_OK = 0,
@@ -134,6 +134,26 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
 int lid_scores(const lid_shape* shape, const void* q, const void* k, const float* w,
                const uint16_t* mask, const int32_t* kv_range, float* scores, int64_t scores_ld,
                void* stream);
+
+/* The fused score + mask + top-k with FP8 q and k (shape->qk_dtype ==
+ * LID_F8E4M3): q and k hold OCP FP8 E4M3 bytes (E4M3FN: bias 7, no
+ * infinities, S.1111.111 NaN), dequantised per row,
+ *   q[t,h,:] = e4m3(q8[t,h,:]) * q_scale[t,h],   k[s,:] = e4m3(k8[s,:]) * k_scale[s],
+ * and then scored and selected exactly as lid_topk does.  The pages quantise
+ * the DeepSeek-V4 indexer to FP4 after a Hadamard rotation (ggml-org
+ * llama.cpp PR 22378, the batched-prefill commit) and its KV cache to FP8
+ * E4M3 (the DSV4 CUDA-kernel plan, "dsv4_fp8_kv_quantize"), but give no scale
+ * convention for the indexer: this per-row one is this library's.
+ *   q_scale  [n_tok, H] f32, > 0 and finite
+ *   k_scale  [n_kv]     f32, > 0 and finite
+ * Other arguments as for lid_topk (workspace: lid_topk_workspace_size of the
+ * same shape).  H = 64, D = 128 with at most 4 queries runs on the decode
+ * MFMA kernel (128 bytes per key instead of 256); other shapes on the
+ * vector-ALU kernel; LID_PLAN_PREFILL is LID_ERR_UNSUPPORTED. */
+int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, const void* k,
+                 const float* k_scale, const float* w, const uint16_t* mask,
+                 const int32_t* kv_range, int32_t* idx, float* score, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /* The plan lid_topk would run for `shape` (a lid_plan value), and through
  * `splits_out` (may be NULL) its key splits per query; negative lid_status if

@@ -22,13 +22,13 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblid.so")
 
-LID_F32, LID_F16, LID_BF16 = 0, 1, 2
+LID_F32, LID_F16, LID_BF16, LID_F8E4M3 = 0, 1, 2, 3
 PLAN_AUTO, PLAN_GENERIC, PLAN_PREFILL, PLAN_DECODE = 0, 1, 2, 3
 PLAN_NAMES = {PLAN_GENERIC: "generic", PLAN_PREFILL: "prefill", PLAN_DECODE: "decode"}
 STATUS = {0: "LID_OK", -1: "LID_ERR_INVALID_ARG", -2: "LID_ERR_UNSUPPORTED", -3: "LID_ERR_WORKSPACE",
           -4: "LID_ERR_HIP"}
-EXPORTS = ("lid_topk", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores", "lid_status_string",
-           "lid_last_hip_error", "lid_set_profile_events", "lid_version")
+EXPORTS = ("lid_topk", "lid_topk_fp8", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores",
+           "lid_status_string", "lid_last_hip_error", "lid_set_profile_events", "lid_version")
 
 
 class LidShape(ctypes.Structure):
@@ -67,6 +67,9 @@ def load():
         lib.lid_topk.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lid_topk_workspace_size.restype = ctypes.c_size_t
         lib.lid_topk_workspace_size.argtypes = [ctypes.POINTER(LidShape)]
+        lib.lid_topk_fp8.restype = ctypes.c_int
+        lib.lid_topk_fp8.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
         lib.lid_scores.restype = ctypes.c_int
         lib.lid_scores.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
         lib.lid_topk_plan.restype = ctypes.c_int
@@ -103,7 +106,8 @@ def plan_of(shape: LidShape):
 
 def _dtype_code(t):
     import torch
-    return {torch.float16: LID_F16, torch.bfloat16: LID_BF16, torch.float32: LID_F32}[t.dtype]
+    return {torch.float16: LID_F16, torch.bfloat16: LID_BF16, torch.float32: LID_F32,
+            torch.float8_e4m3fn: LID_F8E4M3}[t.dtype]
 
 
 def shape_for(q, k, k_top, mask=None, plan=PLAN_AUTO, splits=0) -> LidShape:
@@ -117,8 +121,10 @@ def _ptr(t):
 
 
 def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits=0, idx=None, score=None,
-         want_score=True, workspace=None, stream=None):
-    """Fused score + mask + top-k on the GPU (see module docstring)."""
+         want_score=True, workspace=None, stream=None, q_scale=None, k_scale=None):
+    """Fused score + mask + top-k on the GPU (see module docstring).  With
+    float8_e4m3fn q and k, q_scale [n_tok, H] and k_scale [n_kv] (f32) are
+    their per-row scales (lid_topk_fp8)."""
     import torch
     if q.dim() != 3 or k.dim() != 2 or w.dim() != 2:
         raise ValueError("q [n_tok,H,D], k [n_kv,D], w [n_tok,H] expected")
@@ -136,6 +142,15 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
             raise ValueError("mask must be float16 [n_tok, mask_ld]")
     if kv_range is not None and (kv_range.dtype != torch.int32 or tuple(kv_range.shape) != (n_tok, 2)):
         raise ValueError("kv_range must be int32 [n_tok, 2]")
+    fp8 = q.dtype == torch.float8_e4m3fn
+    if fp8:
+        if q_scale is None or k_scale is None:
+            raise ValueError("FP8 q and k need q_scale [n_tok, H] and k_scale [n_kv]")
+        for name, t, shp in (("q_scale", q_scale, (n_tok, H)), ("k_scale", k_scale, (k.shape[0],))):
+            if t.dtype != torch.float32 or tuple(t.shape) != shp or t.device != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 tensor {shp} on {dev}")
+    elif q_scale is not None or k_scale is not None:
+        raise ValueError("q_scale / k_scale go with float8_e4m3fn q and k only")
     shape = shape_for(q, k, k_top, mask, plan, splits)
     if idx is None:
         idx = torch.empty((n_tok, k_top), dtype=torch.int32, device=dev)
@@ -149,8 +164,12 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = load().lid_topk(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(mask), _ptr(kv_range), _ptr(idx),
-                         _ptr(score), _ptr(workspace), ws_have, stream)
+    if fp8:
+        rc = load().lid_topk_fp8(ctypes.byref(shape), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
+                                 _ptr(mask), _ptr(kv_range), _ptr(idx), _ptr(score), _ptr(workspace), ws_have, stream)
+    else:
+        rc = load().lid_topk(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(mask), _ptr(kv_range), _ptr(idx),
+                             _ptr(score), _ptr(workspace), ws_have, stream)
     if rc != 0:
         raise LidError(rc)
     return idx, score

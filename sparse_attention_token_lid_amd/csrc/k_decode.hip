@@ -50,6 +50,15 @@ template <> struct Mfma<2> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
 };
+// OCP FP8 E4M3 in both operands, K = 64 per instruction (format codes 0, 0;
+// no block scales)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <> struct Mfma<3> {
+  typedef i32x8 T;
+  static __device__ __forceinline__ f32x16 run(T a, T b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
 
 constexpr int H = kMfmaHeads;
 constexpr int D = kMfmaDim;
@@ -355,8 +364,6 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
 // ------------------------------------------------------------------- kernel
 template <int DT, bool RAW>
 __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg, int ch) {
-  using M = Mfma<DT>;
-  using T = typename M::T;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* stage_all = reinterpret_cast<uint16_t*>(smem);           // [NW][KB * D]
   uint64_t* arr = reinterpret_cast<uint64_t*>(smem + kStageBytes);   // [keys_per_wg] (lists form)
@@ -383,92 +390,190 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   const int64_t b0 = nblk * p / P, b1 = nblk * (p + 1) / P;
   const int nkeys = (int)((b1 - b0) * KB);  // <= keys_per_wg (host-checked)
 
-  T A[2][8];
-  float wr[2][16];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + t * H * D;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        A[rb][j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j));
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) wr[rb][jj] = a.w[t * H + 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3)];
-  }
-
-  // Key rows past the split (or past n_kv) are clamped to the split's last
-  // row and never stored, so every load is unconditional.  Instruction i of a
-  // block load reads bytes [1024 i, 1024 i + 1024) of the block: lane l gets
-  // row 4 i + l / 16, 16-byte chunk l % 16.
-  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
   const int64_t last_row = hi - 1;
-  uint16_t* stage = stage_all + wv * (KB * D);
   uint32_t* raw = RAW ? a.raw + (size_t)t * a.raw_ld : nullptr;
-  auto load_blk = [&](int64_t b, u32x4 (&f)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t s = lo + b * KB + 4 * i + (lane >> 4);
-      s = s < last_row ? s : last_row;
-      f[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + s * D + (lane & 15) * 8));
-    }
-  };
   auto load_mask = [&](int64_t b) -> uint16_t {
     if (!a.mask) return 0;
     int64_t s = lo + b * KB + m;
     s = s < last_row ? s : last_row;
     return __builtin_nontemporal_load(a.mask + t * a.mask_ld + s);
   };
-  auto score_blk = [&](int64_t b, const u32x4 (&f)[8], uint16_t mbits) {
-    const int64_t s = lo + b * KB + m;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(stage + swz(4 * i + (lane >> 4), lane & 15)) = f[i];
-    f32x16 acc0, acc1;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      T bf = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(stage + swz(m, 8 * g + j)));
-      acc0 = M::run(A[0][j], bf, acc0);
-      acc1 = M::run(A[1][j], bf, acc1);
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      part = __builtin_fmaf(wr[0][e], relu(acc0[e]), part);
-      part = __builtin_fmaf(wr[1][e], relu(acc1[e]), part);
-    }
-    const float tot = part + __uint_as_float(xor_lane_u32<32>(__float_as_uint(part)));
-    const float v = (tot + f16_bits_to_f32(mbits)) + 0.0f;
+  // the masked score v of key s (lane m of the block's first half) goes out
+  auto emit = [&](int64_t b, int64_t s, float v) {
     if (g == 0) {
       const bool valid = s < hi && v != -__builtin_inff();
       if (RAW) __hip_atomic_store(&raw[b * KB + m], valid ? ord_f32(v) : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else arr[(b - b0) * KB + m] = valid ? make_key(v, (uint32_t)s) : 0ull;
     }
   };
-
-  // A ring of kDepth register sets: while a block is scored, the loads of
-  // the next kDepth - 1 blocks of this wave are in flight.
-  if (hi > lo) {
-    u32x4 f[kDepth][8];
-    uint16_t mk[kDepth];
-    const int64_t bs = b0 + wv;
+  // the head reduction of a 32-key block: sum_h w_h relu(acc) over this
+  // lane's 32 heads, then the other 32 (the lanes 32 apart)
+  auto head_sum = [&](const f32x16& acc0, const f32x16& acc1, const float (&wr)[2][16]) -> float {
+    float part = 0.f;
 #pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d) {
-      const int64_t b = bs + d * NW;
-      mk[d] = 0;
-      if (b < b1) { mk[d] = load_mask(b); load_blk(b, f[d]); }
+    for (int e = 0; e < 16; ++e) {
+      part = __builtin_fmaf(wr[0][e], relu(acc0[e]), part);
+      part = __builtin_fmaf(wr[1][e], relu(acc1[e]), part);
     }
-    for (int64_t b = bs; b < b1; b += kDepth * NW) {
+    return part + __uint_as_float(xor_lane_u32<32>(__float_as_uint(part)));
+  };
+
+  if constexpr (DT != 3) {
+    using M = Mfma<DT>;
+    using T = typename M::T;
+    T A[2][8];
+    float wr[2][16];
+    {
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + t * H * D;
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int64_t bc = b + d * NW;  // scored now, from slot d
-        if (bc >= b1) break;
-        const int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
-        if (bl < b1) { mk[(d + kDepth - 1) % kDepth] = load_mask(bl); load_blk(bl, f[(d + kDepth - 1) % kDepth]); }
-        score_blk(bc, f[d], mk[d]);
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          A[rb][j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j));
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) wr[rb][jj] = a.w[t * H + 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3)];
+    }
+
+    // Key rows past the split (or past n_kv) are clamped to the split's last
+    // row and never stored, so every load is unconditional.  Instruction i of a
+    // block load reads bytes [1024 i, 1024 i + 1024) of the block: lane l gets
+    // row 4 i + l / 16, 16-byte chunk l % 16.
+    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
+    uint16_t* stage = stage_all + wv * (KB * D);
+    auto load_blk = [&](int64_t b, u32x4 (&f)[8]) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int64_t s = lo + b * KB + 4 * i + (lane >> 4);
+        s = s < last_row ? s : last_row;
+        f[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + s * D + (lane & 15) * 8));
+      }
+    };
+    auto score_blk = [&](int64_t b, const u32x4 (&f)[8], uint16_t mbits) {
+      const int64_t s = lo + b * KB + m;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(stage + swz(4 * i + (lane >> 4), lane & 15)) = f[i];
+      f32x16 acc0, acc1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        T bf = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(stage + swz(m, 8 * g + j)));
+        acc0 = M::run(A[0][j], bf, acc0);
+        acc1 = M::run(A[1][j], bf, acc1);
+      }
+      const float tot = head_sum(acc0, acc1, wr);
+      emit(b, s, (tot + f16_bits_to_f32(mbits)) + 0.0f);
+    };
+
+    // A ring of kDepth register sets: while a block is scored, the loads of
+    // the next kDepth - 1 blocks of this wave are in flight.
+    if (hi > lo) {
+      u32x4 f[kDepth][8];
+      uint16_t mk[kDepth];
+      const int64_t bs = b0 + wv;
+#pragma unroll
+      for (int d = 0; d < kDepth - 1; ++d) {
+        const int64_t b = bs + d * NW;
+        mk[d] = 0;
+        if (b < b1) { mk[d] = load_mask(b); load_blk(b, f[d]); }
+      }
+      for (int64_t b = bs; b < b1; b += kDepth * NW) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          const int64_t bc = b + d * NW;  // scored now, from slot d
+          if (bc >= b1) break;
+          const int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
+          if (bl < b1) { mk[(d + kDepth - 1) % kDepth] = load_mask(bl); load_blk(bl, f[(d + kDepth - 1) % kDepth]); }
+          score_blk(bc, f[d], mk[d]);
+        }
+      }
+    }
+  } else {
+    // FP8 E4M3 q and k with per-row scales (q_scale [n_tok, H], k_scale
+    // [n_kv], positive): S[h,s] = q_scale[t,h] k_scale[s] (q8 . k8), and since
+    // the scales are positive, I = k_scale[s] sum_h (w[t,h] q_scale[t,h])
+    // relu(q8 . k8).  The MFMA k-index maps to the head dimension as
+    // d = 64 (lane / 32) + 32 j + i (j the instruction, i < 32 the byte).
+    // Key rows are 128 bytes: a 32-key block is 4 KiB, and the ring holds
+    // twice as many blocks, so as many bytes are in flight as for f16.
+    using M = Mfma<3>;
+    M::T A[2][2];
+    float wr[2][16];
+    {
+      const unsigned char* qrow = reinterpret_cast<const unsigned char*>(a.q) + t * H * D;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const unsigned char* p = qrow + (32 * rb + m) * D + 64 * g + 32 * j;
+          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(p), hi4 = *reinterpret_cast<const u32x4*>(p + 16);
+          A[rb][j] = M::T{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3], (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int h = 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3);
+          wr[rb][jj] = a.w[t * H + h] * a.q_scale[t * H + h];
+        }
+    }
+    constexpr int kRow8 = D;                  // bytes per key row
+    constexpr int kDepth8 = 2 * kDepth;
+    const unsigned char* kb8 = reinterpret_cast<const unsigned char*>(a.k);
+    unsigned char* stage8 = reinterpret_cast<unsigned char*>(stage_all) + wv * (KB * kRow8);
+    // LDS: 16-byte chunk c of row r at r * 128 + ((c ^ (r & 7)) << 4)
+    auto swz8 = [](int r, int c) { return r * kRow8 + ((c ^ (r & 7)) << 4); };
+    // instruction i of a block load: lane l reads row 8 i + l / 8, chunk l % 8
+    auto load_blk8 = [&](int64_t b, u32x4 (&f)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int64_t s = lo + b * KB + 8 * i + (lane >> 3);
+        s = s < last_row ? s : last_row;
+        f[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb8 + s * kRow8 + (lane & 7) * 16));
+      }
+    };
+    auto score_blk8 = [&](int64_t b, const u32x4 (&f)[4], uint16_t mbits) {
+      const int64_t s = lo + b * KB + m;
+      const float ks = a.k_scale[s < last_row ? s : last_row];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(stage8 + swz8(8 * i + (lane >> 3), lane & 7)) = f[i];
+      f32x16 acc0, acc1;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = 4 * g + 2 * j;
+        const u32x4 b0v = *reinterpret_cast<const u32x4*>(stage8 + swz8(m, c));
+        const u32x4 b1v = *reinterpret_cast<const u32x4*>(stage8 + swz8(m, c + 1));
+        const M::T bf = {(int)b0v[0], (int)b0v[1], (int)b0v[2], (int)b0v[3], (int)b1v[0], (int)b1v[1], (int)b1v[2], (int)b1v[3]};
+        acc0 = M::run(A[0][j], bf, acc0);
+        acc1 = M::run(A[1][j], bf, acc1);
+      }
+      const float tot = head_sum(acc0, acc1, wr);
+      emit(b, s, (tot * ks + f16_bits_to_f32(mbits)) + 0.0f);
+    };
+    if (hi > lo) {
+      u32x4 f[kDepth8][4];
+      uint16_t mk[kDepth8];
+      const int64_t bs = b0 + wv;
+#pragma unroll
+      for (int d = 0; d < kDepth8 - 1; ++d) {
+        const int64_t b = bs + d * NW;
+        mk[d] = 0;
+        if (b < b1) { mk[d] = load_mask(b); load_blk8(b, f[d]); }
+      }
+      for (int64_t b = bs; b < b1; b += kDepth8 * NW) {
+#pragma unroll
+        for (int d = 0; d < kDepth8; ++d) {
+          const int64_t bc = b + d * NW;
+          if (bc >= b1) break;
+          const int64_t bl = bc + (kDepth8 - 1) * NW;
+          if (bl < b1) { mk[(d + kDepth8 - 1) % kDepth8] = load_mask(bl); load_blk8(bl, f[(d + kDepth8 - 1) % kDepth8]); }
+          score_blk8(bc, f[d], mk[d]);
+        }
       }
     }
   }
@@ -543,6 +648,7 @@ size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw) {
 
 hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, bool raw, hipStream_t st) {
   if (a.dtype == 1) return raw ? launch_one<1, true>(a, keys_per_wg, ch, st) : launch_one<1, false>(a, keys_per_wg, ch, st);
+  if (a.dtype == 3) return raw ? launch_one<3, true>(a, keys_per_wg, ch, st) : launch_one<3, false>(a, keys_per_wg, ch, st);
   return raw ? launch_one<2, true>(a, keys_per_wg, ch, st) : launch_one<2, false>(a, keys_per_wg, ch, st);
 }
 

@@ -1,5 +1,6 @@
 // k_generic.hip -- vector-ALU scoring for any head count, head size and dtype
-// (f32, f16, bf16), with the same streaming top-k as the MFMA kernels.
+// (f32, f16, bf16, FP8 E4M3 with per-row scales), with the same streaming
+// top-k as the MFMA kernels.
 //
 // The score is the indexer chain of ggml-org llama.cpp issue 25468 ("Root
 // cause" comment): I = sum_h w_h * max(0, q_h . k), plus the f16 mask.  One
@@ -17,6 +18,7 @@ constexpr int NWG = 4;  // wavefronts per workgroup
 
 __device__ __forceinline__ float load_qk(const void* p, int64_t i, int dtype) {
   if (dtype == 0) return reinterpret_cast<const float*>(p)[i];
+  if (dtype == 3) return e4m3_to_f32(reinterpret_cast<const uint8_t*>(p)[i]);
   const uint16_t b = reinterpret_cast<const uint16_t*>(p)[i];
   if (dtype == 1) return f16_bits_to_f32(b);
   return __uint_as_float((uint32_t)b << 16);
@@ -58,8 +60,11 @@ __global__ __launch_bounds__(NWG * 64) void generic_kernel(KArgs a) {
         float dot = 0.f;
         const int64_t qo = (t * H + h) * (int64_t)D;
         for (int d = 0; d < D; ++d) dot = __builtin_fmaf(load_qk(a.q, qo + d, a.dtype), load_qk(a.k, s * D + d, a.dtype), dot);
-        I = __builtin_fmaf(a.w[t * H + h], relu(dot), I);
+        // FP8: positive per-row scales commute with the ReLU
+        const float wh = a.dtype == 3 ? a.w[t * H + h] * a.q_scale[t * H + h] : a.w[t * H + h];
+        I = __builtin_fmaf(wh, relu(dot), I);
       }
+      if (a.dtype == 3) I *= a.k_scale[s];
       float mv = a.mask ? f16_bits_to_f32(a.mask[t * a.mask_ld + s]) : 0.f;
       v = (I + mv) + 0.0f;
     }

@@ -59,7 +59,8 @@ int check_shape(const lid_shape* s) {
   if (!s) return LID_ERR_INVALID_ARG;
   if (s->n_tok < 0 || s->n_kv < 0 || s->n_kv > INT32_MAX || s->n_tok > INT32_MAX) return LID_ERR_INVALID_ARG;
   if (s->n_head < 1 || s->head_dim < 1 || s->k_top < 1) return LID_ERR_INVALID_ARG;
-  if (s->qk_dtype != LID_F32 && s->qk_dtype != LID_F16 && s->qk_dtype != LID_BF16) return LID_ERR_INVALID_ARG;
+  if (s->qk_dtype != LID_F32 && s->qk_dtype != LID_F16 && s->qk_dtype != LID_BF16 && s->qk_dtype != LID_F8E4M3)
+    return LID_ERR_INVALID_ARG;
   if (s->plan < LID_PLAN_AUTO || s->plan > LID_PLAN_DECODE || s->splits < 0) return LID_ERR_INVALID_ARG;
   if (s->k_top > kMaxTopK || s->splits > kMaxSplits) return LID_ERR_UNSUPPORTED;
   return LID_OK;
@@ -69,17 +70,20 @@ int make_plan(const lid_shape* s, Plan* pl) {
   int rc = check_shape(s);
   if (rc) return rc;
   const int K = s->k_top;
-  const bool mfma_ok = (s->qk_dtype == LID_F16 || s->qk_dtype == LID_BF16) && s->n_head == kMfmaHeads &&
-                       s->head_dim == kMfmaDim;
+  const bool mfma_shape = s->n_head == kMfmaHeads && s->head_dim == kMfmaDim;
+  const bool fp8 = s->qk_dtype == LID_F8E4M3;
+  // FP8 has an MFMA path in the decode kernel only
+  const bool mfma_ok = (s->qk_dtype == LID_F16 || s->qk_dtype == LID_BF16 || fp8) && mfma_shape;
   memset(pl, 0, sizeof(*pl));
   pl->cap = 2 * K + 192;
   int kind = s->plan;
   if (kind == LID_PLAN_AUTO) {
     if (!mfma_ok) kind = LID_PLAN_GENERIC;
     else if (s->n_tok <= kDecodeMaxTok && cdiv(s->n_kv, kDecodeMaxSplits) <= kDecodeMaxKeys) kind = LID_PLAN_DECODE;
-    else kind = LID_PLAN_PREFILL;
+    else kind = fp8 ? LID_PLAN_GENERIC : LID_PLAN_PREFILL;
   }
   if ((kind == LID_PLAN_PREFILL || kind == LID_PLAN_DECODE) && !mfma_ok) return LID_ERR_UNSUPPORTED;
+  if (kind == LID_PLAN_PREFILL && fp8) return LID_ERR_UNSUPPORTED;
   pl->kind = kind;
 
   if (kind == LID_PLAN_GENERIC) {
@@ -174,13 +178,18 @@ int lid_topk_plan(const lid_shape* shape, int32_t* splits_out) {
   return pl.kind;
 }
 
-int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
-             const int32_t* kv_range, int32_t* idx, float* score, void* workspace, size_t workspace_bytes,
-             void* stream) {
+}  // extern "C"
+
+namespace {
+
+int topk_impl(const lid_shape* shape, const void* q, const float* q_scale, const void* k, const float* k_scale,
+              const float* w, const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
+              void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
   int rc = make_plan(shape, &pl);
   if (rc != LID_OK) return rc;
   const lid_shape& s = *shape;
+  if ((s.qk_dtype == LID_F8E4M3) != (q_scale != nullptr && k_scale != nullptr)) return LID_ERR_INVALID_ARG;
   if (s.n_tok == 0) return LID_OK;
   if (!q || !w || !idx || (s.n_kv > 0 && !k)) return LID_ERR_INVALID_ARG;
   if (mask && s.mask_ld < s.n_kv) return LID_ERR_INVALID_ARG;
@@ -195,6 +204,8 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   a.q = q;
   a.k = k;
   a.w = w;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
   a.mask = mask;
   a.kv_range = kv_range;
   a.idx = idx;
@@ -233,9 +244,27 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
   return LID_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
+             const int32_t* kv_range, int32_t* idx, float* score, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return topk_impl(shape, q, nullptr, k, nullptr, w, mask, kv_range, idx, score, workspace, workspace_bytes, stream);
+}
+
+int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, const void* k, const float* k_scale,
+                 const float* w, const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape || shape->qk_dtype != LID_F8E4M3 || !q_scale || !k_scale) return LID_ERR_INVALID_ARG;
+  return topk_impl(shape, q, q_scale, k, k_scale, w, mask, kv_range, idx, score, workspace, workspace_bytes, stream);
+}
+
 int lid_scores(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
                const int32_t* kv_range, float* scores, int64_t scores_ld, void* stream) {
   if (!shape) return LID_ERR_INVALID_ARG;
+  if (shape->qk_dtype == LID_F8E4M3) return LID_ERR_UNSUPPORTED;  // (no scale arguments here)
   // the scoring plan: the prefill kernel's key splits (k_top does not matter)
   lid_shape ps = *shape;
   ps.k_top = 512;

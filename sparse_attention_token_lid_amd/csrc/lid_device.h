@@ -43,6 +43,18 @@ __device__ __forceinline__ float key_score(uint64_t key) {
 // a NaN-quieting canonicalisation of every MFMA result first.
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
 
+// OCP FP8 E4M3 (E4M3FN) byte -> f32 (exact), from the format definition:
+// sign, 4 exponent bits (bias 7), 3 fraction bits; exponent 0 is subnormal
+// (m * 2^-9); S.1111.111 is NaN; no infinities.
+__device__ __forceinline__ float e4m3_to_f32(uint8_t x) {
+  const uint32_t sg = (uint32_t)(x & 0x80) << 24, e = (x >> 3) & 15, m = x & 7;
+  float v;
+  if (e == 0) v = (float)m * 0.001953125f;                                 // m * 2^-9
+  else if (e == 15 && m == 7) v = __uint_as_float(0x7FC00000u);
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));               // (1 + m/8) 2^(e-7)
+  return __uint_as_float(__float_as_uint(v) | sg);
+}
+
 // f16 mask bits -> f32 (exact)
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   _Float16 x = __builtin_bit_cast(_Float16, h);

@@ -11,6 +11,8 @@ struct KArgs {
   const void* q;            // [n_tok, H, D] f32 / f16 bits / bf16 bits
   const void* k;            // [n_kv, D]
   const float* w;           // [n_tok, H]
+  const float* q_scale;     // FP8 (dtype 3): [n_tok, H] per-row scale of q, else null
+  const float* k_scale;     // FP8 (dtype 3): [n_kv] per-row scale of k, else null
   const uint16_t* mask;     // [n_tok, mask_ld] f16 bits, or null
   const int32_t* kv_range;  // [n_tok, 2], or null
   int32_t* idx;             // [n_tok, K]
@@ -24,7 +26,7 @@ struct KArgs {
   int64_t n_tok, n_kv, mask_ld, raw_ld;
   int32_t H, D, K, P;
   int32_t cap;              // per-wave candidate buffer capacity (entries)
-  int32_t dtype;            // 0 f32, 1 f16, 2 bf16
+  int32_t dtype;            // 0 f32, 1 f16, 2 bf16, 3 FP8 E4M3 (with q_scale, k_scale)
   int32_t fuse;             // prefill, P > 1: the last workgroup of a query block finishes the
                             // query's top-k from the split lists: 1 = sorted lists merged,
                             // 2 = unsorted lists selected from (P K <= 64 kFuseSelectRows)

@@ -137,3 +137,21 @@ def test_scores_errors_before_launch(L):
     assert sc(ok, q=8) == -1                                   # MFMA path needs 16-byte aligned q, k
     assert sc(shape_of("c3", mask_ld=5), mask=16) == -1        # mask stride below n_kv
     assert sc(shape_of("c3", n_tok=0)) == 0                    # nothing to do
+
+
+def test_fp8_entry_errors(L):
+    """FP8 shapes: lid_topk refuses them (no scales), lid_topk_fp8 needs both
+    scales and takes no prefill plan, and lid_scores does not take FP8."""
+    lib = L.load()
+    s8 = shape_of("c2", qk_dtype=L.LID_F8E4M3)
+    assert L.plan_of(s8)[0] == "decode"
+    assert L.plan_of(shape_of("c3", qk_dtype=L.LID_F8E4M3))[0] == "generic"
+    ws = L.workspace_size(s8)
+    assert call(L, s8, ws=16, ws_bytes=ws) == -1                      # lid_topk: FP8 needs the scales
+    f = lib.lid_topk_fp8
+    assert f(ctypes.byref(s8), 16, None, 16, 16, 16, None, None, 16, None, 16, ws, None) == -1
+    assert f(ctypes.byref(shape_of("c2")), 16, 16, 16, 16, 16, None, None, 16, None, 16, ws, None) == -1
+    sp = shape_of("c3", qk_dtype=L.LID_F8E4M3, plan=L.PLAN_PREFILL)
+    assert f(ctypes.byref(sp), 16, 16, 16, 16, 16, None, None, 16, None, None, 0, None) == -2
+    assert lib.lid_scores(ctypes.byref(s8), 16, 16, 16, None, None, 16, s8.n_kv, None) == -2
+

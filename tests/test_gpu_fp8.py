@@ -1,0 +1,118 @@
+"""GPU parity of the FP8 path (lid_topk_fp8): OCP E4M3 q and k with per-row
+scales, against the oracle's FP8 definition.  Every test here needs an
+MI355X and the built liblid.so."""
+import sys
+
+import numpy as np
+import pytest
+
+import lid_inputs as li
+from parity import REL_TOL, check_rows, oracle_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lid():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_lid_amd as L
+    L.load()
+    return L
+
+
+def quantise(x, axis_rows):
+    """f32 array -> (E4M3 bytes, per-row f32 scales): scale = max|row| / 448,
+    bytes = round-to-nearest-even E4M3 of x / scale (torch's conversion)."""
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    red = tuple(range(axis_rows, xt.dim()))
+    scale = xt.abs().amax(dim=red).clamp(min=1e-20) / 448.0
+    shp = scale.shape + (1,) * len(red)
+    b = (xt / scale.reshape(shp)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return b, scale.numpy().astype(np.float32)
+
+
+def small_int_fp8(rng, shape):
+    """E4M3 bytes of small integers in {-2, ..., 2} (exact in E4M3)."""
+    v = rng.integers(-2, 3, shape).astype(np.float32)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def run_fp8(lid, q8, qs, k8, ks, w, mask, ranges, k_top, plan=0, splits=0):
+    dev = "cuda"
+    qd = torch.from_numpy(q8).to(dev).view(torch.float8_e4m3fn)
+    kd = torch.from_numpy(k8).to(dev).view(torch.float8_e4m3fn)
+    md = None if mask is None else torch.from_numpy(mask.view(np.int16)).to(dev).view(torch.float16)
+    rd = None if ranges is None else torch.from_numpy(ranges).to(dev)
+    idx, sc = lid.topk(qd, kd, torch.from_numpy(w).to(dev), mask=md, kv_range=rd, k_top=k_top, plan=plan,
+                       splits=splits, q_scale=torch.from_numpy(qs).to(dev), k_scale=torch.from_numpy(ks).to(dev))
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def parity_fp8(lid, q8, qs, k8, ks, w, mask, ranges, k_top, rows=None, exact=False, label="", plan=0, splits=0):
+    _say(f"[fp8] {label} n_tok={q8.shape[0]} n_kv={k8.shape[0]} k_top={k_top} plan={plan} splits={splits}")
+    g_idx, g_sc = run_fp8(lid, q8, qs, k8, ks, w, mask, ranges, k_top, plan, splits)
+    if rows is None:
+        rows = list(range(q8.shape[0]))
+    import oracle
+    o_idx, o_sc, maxabs = oracle.topk(q8, k8, w, mask=mask, kv_range=ranges, k_top=k_top, rows=rows,
+                                      qk_dtype="f8e4m3", q_scale=qs, k_scale=ks)
+    v = oracle.scores(q8, k8, w, mask=mask, kv_range=ranges, rows=rows, qk_dtype="f8e4m3", q_scale=qs, k_scale=ks)
+    tol = REL_TOL["f16"] * maxabs
+    n = check_rows(g_idx[rows], g_sc[rows], o_idx, o_sc, v, tol, rows=rows, exact=exact)
+    _say(f"[fp8]   ok: {n}/{len(rows)} rows with identical index sets, tol={tol:.3g}")
+
+
+@pytest.mark.parametrize("n_kv", [3000, 40000])
+def test_fp8_decode_exact(lid, n_kv):
+    """Decode kernel, raw-score (3000 keys) and split-list (40000 keys) finish:
+    small-integer E4M3 values, power-of-two scales and dyadic weights make
+    every score exact, so indices and scores must match bit for bit."""
+    rng = np.random.default_rng(n_kv)
+    n_tok = 4
+    q8, k8 = small_int_fp8(rng, (n_tok, 64, 128)), small_int_fp8(rng, (n_kv, 128))
+    qs = (2.0 ** rng.integers(-2, 3, (n_tok, 64))).astype(np.float32)
+    ks = (2.0 ** rng.integers(-2, 3, n_kv)).astype(np.float32)
+    w = rng.choice(np.array([0, 0.25, 0.5, 1, 2], np.float32), (n_tok, 64))
+    ranges = np.array([[0, n_kv], [5, n_kv - 1], [n_kv // 3, n_kv // 3 + 700], [0, 0]], np.int32)
+    parity_fp8(lid, q8, qs, k8, ks, w, None, ranges, 512, exact=True, label=f"decode-exact/{n_kv}")
+
+
+@pytest.mark.parametrize("name", ["c2", "dec1m"])
+def test_fp8_decode_workload(lid, name):
+    """c2 / dec1m inputs quantised to E4M3 with per-row max scaling."""
+    d = li.make(name)
+    q8, qs = quantise(d["q"].astype(np.float32), 2)
+    k8, ks = quantise(d["k"].astype(np.float32), 1)
+    parity_fp8(lid, q8, qs, k8, ks, d["w"], None, None, 512, label=f"{name}/fp8")
+
+
+def test_fp8_decode_masked(lid):
+    n_tok, n_kv = 3, 20000
+    wl = li.Workload("t", n_tok, n_kv, 64, 128, 512, "f16", True, "causal")
+    q, k, w = li.draw_qkw(n_tok, n_kv, 64, 128, "f16", True, seed=12)
+    q8, qs = quantise(q.astype(np.float32), 2)
+    k8, ks = quantise(k.astype(np.float32), 1)
+    mask = li.mask_from_ranges(li.visible_ranges(wl), n_kv, mask_ld=n_kv + 16)
+    parity_fp8(lid, q8, qs, k8, ks, w, mask, None, 512, label="decode/mask")
+
+
+@pytest.mark.parametrize("H,D,n_tok", [(4, 32, 9), (64, 128, 9)])
+def test_fp8_generic(lid, H, D, n_tok):
+    """Shapes outside the decode kernel (more than 4 queries, or other H, D)
+    run on the vector-ALU kernel; exact inputs, bit for bit."""
+    rng = np.random.default_rng(H + n_tok)
+    n_kv = 1500
+    q8, k8 = small_int_fp8(rng, (n_tok, H, D)), small_int_fp8(rng, (n_kv, D))
+    qs = (2.0 ** rng.integers(-2, 3, (n_tok, H))).astype(np.float32)
+    ks = (2.0 ** rng.integers(-2, 3, n_kv)).astype(np.float32)
+    w = rng.choice(np.array([0, 0.25, 0.5, 1, -0.5], np.float32), (n_tok, H))
+    parity_fp8(lid, q8, qs, k8, ks, w, None, None, 100, exact=True, label=f"generic/H{H}")
