@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(DEFAULT_STEPS))
     ap.add_argument("--form", default=None, choices=["none", "mask", "ranges"])
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--qk", default="f16", choices=["f16", "fp8"],
+                    help="f16: the workload's f16 q and k (the default); fp8: the same values quantised to "
+                         "OCP E4M3 with per-row scales (max |row| / 448), run through lid_topk_fp8")
     ap.add_argument("--mode", default="topk", choices=["topk", "scores"],
                     help="topk: the fused top-k (the default); scores: the score-only mode (lid_scores), "
                          "which writes the n_tok x n_kv f32 scores")
@@ -195,11 +198,21 @@ def main():
     w0 = torch.from_numpy(d["w"]).to(dev)
     m0 = dev_tensor(d["mask"], "f16bits") if form == "mask" else None
     r0 = torch.from_numpy(d["ranges"]).to(dev) if form == "ranges" else None
-    per_copy = sum(t.numel() * t.element_size() for t in (q0, k0, w0, m0, r0) if t is not None)
+    fp8 = args.qk == "fp8"
+    qs0 = ks0 = None
+    if fp8:
+        if args.mode != "topk":
+            raise SystemExit("--qk fp8 goes with --mode topk")
+        # per-row max scaling to E4M3 (synthetic inputs: the pages give no indexer scale convention)
+        qs0 = q0.float().abs().amax(dim=2).clamp(min=1e-20) / 448.0
+        ks0 = k0.float().abs().amax(dim=1).clamp(min=1e-20) / 448.0
+        q0 = (q0.float() / qs0[:, :, None]).to(torch.float8_e4m3fn)
+        k0 = (k0.float() / ks0[:, None]).to(torch.float8_e4m3fn)
+    per_copy = sum(t.numel() * t.element_size() for t in (q0, k0, w0, m0, r0, qs0, ks0) if t is not None)
     copies = max(1, min(64, math.ceil((1 << 30) / per_copy)))
-    sets = [(q0, k0, w0, m0, r0)]
+    sets = [(q0, k0, w0, m0, r0, qs0, ks0)]
     for _ in range(copies - 1):
-        sets.append(tuple(None if t is None else t.clone() for t in (q0, k0, w0, m0, r0)))
+        sets.append(tuple(None if t is None else t.clone() for t in (q0, k0, w0, m0, r0, qs0, ks0)))
     shape = L.shape_for(q0, k0, wl.k_top, m0, splits=args.splits)
     plan, splits = L.plan_of(shape)
     ws_bytes = L.workspace_size(shape)
@@ -215,16 +228,19 @@ def main():
         plan, splits = "prefill (score-only)", L.plan_of(pshape)[1]
         ws_bytes = 0
     calls = []
-    for (q, k, w, m, r) in sets:
+    for (q, k, w, m, r, qs, ks) in sets:
         ptrs = [t.data_ptr() if t is not None else None for t in (q, k, w, m, r)]
         if scores_mode:
             calls.append((ctypes.byref(shape), *ptrs, sout.data_ptr(), wl.n_kv, stream))
+        elif fp8:
+            calls.append((ctypes.byref(shape), ptrs[0], qs.data_ptr(), ptrs[1], ks.data_ptr(), *ptrs[2:],
+                          idx.data_ptr(), sc.data_ptr(), ws.data_ptr(), ws_bytes, stream))
         else:
             calls.append((ctypes.byref(shape), *ptrs, idx.data_ptr(), sc.data_ptr(), ws.data_ptr(), ws_bytes,
                           stream))
     log(f"[bench] mode={args.mode} plan={plan} splits={splits} workspace={ws_bytes} B copies={copies} "
         f"({per_copy / 2**20:.1f} MiB each) steps={steps} warmup={warmup}")
-    entry = lib.lid_scores if scores_mode else lib.lid_topk
+    entry = lib.lid_scores if scores_mode else (lib.lid_topk_fp8 if fp8 else lib.lid_topk)
 
     def step(i):
         rc = entry(*calls[i % copies])
@@ -327,12 +343,13 @@ def main():
                     "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s", "frac": f_hbm, "traffic": None,
                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": in_bytes + out_bytes}
     elif plan == "decode":
-        key_bytes = pairs * D * 2
-        alg_bytes = key_bytes + wl.n_tok * (H * D * 2 + H * 4) + (pairs * 2 if form == "mask" else 0) \
+        eb = 1 if fp8 else 2   # bytes per q / k element
+        key_bytes = pairs * (D * eb + (4 if fp8 else 0))
+        alg_bytes = key_bytes + wl.n_tok * (H * D * eb + H * (8 if fp8 else 4)) + (pairs * 2 if form == "mask" else 0) \
             + wl.n_tok * K * 8
         achieved = alg_bytes / (kern_ms * 1e-3)
         roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_BPS, "traffic": stored_traffic(name, plan, splits),
+                "frac": achieved / PEAK_HBM_BPS, "traffic": None if fp8 else stored_traffic(name, plan, splits),
                 "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": alg_bytes}
     else:
         flops = 2.0 * H * D * pairs
@@ -343,7 +360,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic",
+        "dtype": "f8e4m3" if fp8 else wl.dtype, "data": "synthetic",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}", "n_tok": wl.n_tok, "n_kv": wl.n_kv, "n_head": H,
                    "head_dim": D, "k_top": K, "visible_pairs": pairs, "visibility": form, "plan": plan,
                    "splits": splits, "workspace_bytes": ws_bytes, "parallelism": "single GPU", "mode": args.mode},
@@ -354,7 +371,7 @@ def main():
         "kernel_hash": kernel_source_hash(),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not scores_mode:
+    if not args.no_cpu_baseline and not scores_mode and not fp8:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(d, form, args.cpu_seconds)
     print(json.dumps(out), flush=True)
