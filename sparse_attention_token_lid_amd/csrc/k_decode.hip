@@ -77,7 +77,7 @@ constexpr int kCandMax = 4096;        // candidates gathered into LDS for the ex
 #ifndef LID_DECODE_DEPTH
 #define LID_DECODE_DEPTH 2
 #endif
-constexpr int kDepth = LID_DECODE_DEPTH;  // key blocks per wave in registers (1 scored + kDepth - 1 loading)
+constexpr int kRingDepth = LID_DECODE_DEPTH;  // key blocks per wave in registers (1 scored + the rest loading)
 static_assert(kCandMax == 8 * kTreeCap, "the merge tree takes up to 8 chunks of kTreeCap candidates");
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * D + ((ch ^ (row & 15)) << 3); }
@@ -362,7 +362,88 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
 }
 
 // ------------------------------------------------------------------- kernel
-template <int DT, bool RAW>
+// Forms of the per-query finish (chosen by the host, see lid_api.hip).
+constexpr int kFormLists = 0;  // every split writes its sorted k_top best; the last merges them
+constexpr int kFormRaw = 1;    // every split writes raw ordered scores; the last selects from all
+constexpr int kFormTops = 2;   // every split writes its sorted kDecodeTopsC best; the last merges
+                               // them and re-scores a split only when its summary is too short
+constexpr int kTopsC = kDecodeTopsC;
+static_assert(NW * kTopsC == 2 * kWave, "the split summary combines two keys per lane");
+constexpr int kTopsBuf = kWave - kTopsC;             // candidate slots per wavefront
+constexpr int kTopsArrMin = NW * kTopsC + NW * kTopsBuf;  // summaries + buffers
+
+// LDS of the tops form.  The stage region (scoring) also holds the merge
+// tree's candidates and its second buffer; `arr` holds the wave summaries and
+// the wavefronts' candidate buffers in the scoring pass, and a re-scored
+// split in the finish.
+struct TopsLds {
+  size_t arr, best, sh, red, lastc, flags, ints, total;
+};
+__host__ __device__ inline TopsLds tops_lds(int keys_per_wg, int P) {
+  static_assert((size_t)kStageBytes >= (4096 + 2048) * 8, "tree buffers fit the stage region");
+  TopsLds L;
+  size_t o = kStageBytes;
+  L.arr = o;
+  o += (size_t)(keys_per_wg > kTopsArrMin ? keys_per_wg : kTopsArrMin) * 8;
+  L.best = o;
+  o += (size_t)kTreeCap * 8;
+  L.sh = o;
+  o += (sizeof(BlockShared) + 15) & ~(size_t)15;
+  L.red = o;
+  o += (size_t)(4 * NW + 8) * 4;
+  o = (o + 7) & ~(size_t)7;
+  L.lastc = o;
+  o += (size_t)P * 8;
+  L.flags = o;
+  o += (size_t)P;
+  o = (o + 15) & ~(size_t)15;
+  L.ints = o;
+  o += 32;
+  L.total = o;
+  return L;
+}
+
+// A wavefront's running best kTopsC keys while it streams: the kept keys
+// (lanes 0 .. kTopsC-1 of `top`, descending, 0 = empty), their smallest
+// (th), and a buffer of up to kTopsBuf candidates above th in LDS.  A block's
+// keys (in lanes 32..63; lanes 0..31 hold the same keys) that beat th are
+// appended to the buffer; when it would overflow, the kept keys and the
+// buffer are sorted in registers (one key per lane) and the best kTopsC kept,
+// which raises th.  On random data a wavefront sorts a few times per split.
+struct TopsState {
+  uint64_t top;    // lanes 0 .. kTopsC-1
+  uint64_t th;     // wave-uniform: the kTopsC-th kept key (0 while fewer are kept)
+  int nbuf;        // wave-uniform
+  uint64_t* buf;   // [kTopsBuf] this wavefront's LDS buffer
+};
+__device__ __forceinline__ void tops_flush(TopsState& st, int lane) {
+  __builtin_amdgcn_wave_barrier();
+  uint64_t x[1] = {lane < kTopsC ? st.top : (lane - kTopsC < st.nbuf ? st.buf[lane - kTopsC] : 0ull)};
+  wave_sort_reg<1>(x, lane);
+  st.top = x[0];
+  st.nbuf = 0;
+  const uint32_t thi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x[0] >> 32), kTopsC - 1);
+  const uint32_t tlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x[0], kTopsC - 1);
+  st.th = ((uint64_t)thi << 32) | tlo;
+  __builtin_amdgcn_wave_barrier();
+}
+__device__ __forceinline__ void tops_insert(TopsState& st, uint64_t key, int lane) {
+  bool c = lane >= 32 && key > st.th;
+  uint64_t mk = ballot(c);
+  if (mk == 0ull) return;
+  int n = __popcll(mk);
+  if (st.nbuf + n > kTopsBuf) {
+    tops_flush(st, lane);
+    c = lane >= 32 && key > st.th;
+    mk = ballot(c);
+    if (mk == 0ull) return;
+    n = __popcll(mk);
+  }
+  if (c) st.buf[st.nbuf + mbcnt(mk)] = key;
+  st.nbuf += n;
+}
+
+template <int DT, int FORM>
 __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg, int ch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* stage_all = reinterpret_cast<uint16_t*>(smem);           // [NW][KB * D]
@@ -372,6 +453,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   BlockShared* sh = reinterpret_cast<BlockShared*>(tmp + 2 * BS);
   uint32_t* s_last = reinterpret_cast<uint32_t*>(sh + 1);
 
+  const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane >> 5, m = lane & 31;
@@ -391,21 +473,6 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   const int nkeys = (int)((b1 - b0) * KB);  // <= keys_per_wg (host-checked)
 
   const int64_t last_row = hi - 1;
-  uint32_t* raw = RAW ? a.raw + (size_t)t * a.raw_ld : nullptr;
-  auto load_mask = [&](int64_t b) -> uint16_t {
-    if (!a.mask) return 0;
-    int64_t s = lo + b * KB + m;
-    s = s < last_row ? s : last_row;
-    return __builtin_nontemporal_load(a.mask + t * a.mask_ld + s);
-  };
-  // the masked score v of key s (lane m of the block's first half) goes out
-  auto emit = [&](int64_t b, int64_t s, float v) {
-    if (g == 0) {
-      const bool valid = s < hi && v != -__builtin_inff();
-      if (RAW) __hip_atomic_store(&raw[b * KB + m], valid ? ord_f32(v) : 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else arr[(b - b0) * KB + m] = valid ? make_key(v, (uint32_t)s) : 0ull;
-    }
-  };
   // the head reduction of a 32-key block: sum_h w_h relu(acc) over this
   // lane's 32 heads, then the other 32 (the lanes 32 apart)
   auto head_sum = [&](const f32x16& acc0, const f32x16& acc1, const float (&wr)[2][16]) -> float {
@@ -418,168 +485,238 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     return part + __uint_as_float(xor_lane_u32<32>(__float_as_uint(part)));
   };
 
-  if constexpr (DT != 3) {
-    using M = Mfma<DT>;
-    using T = typename M::T;
-    T A[2][8];
-    float wr[2][16];
-    {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + t * H * D;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          A[rb][j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j));
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) wr[rb][jj] = a.w[t * H + 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3)];
-    }
-
-    // Key rows past the split (or past n_kv) are clamped to the split's last
-    // row and never stored, so every load is unconditional.  Instruction i of a
-    // block load reads bytes [1024 i, 1024 i + 1024) of the block: lane l gets
-    // row 4 i + l / 16, 16-byte chunk l % 16.
-    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k);
-    uint16_t* stage = stage_all + wv * (KB * D);
-    auto load_blk = [&](int64_t b, u32x4 (&f)[8]) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int64_t s = lo + b * KB + 4 * i + (lane >> 4);
-        s = s < last_row ? s : last_row;
-        f[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + s * D + (lane & 15) * 8));
-      }
+  // Scores the 32-key blocks [rb0, rb1) of this query's range: wavefront wv
+  // takes blocks rb0 + wv, rb0 + wv + NW, ...  For every block, every lane
+  // calls sink(b, s, v) with the masked score v of key s = lo + 32 b + lane %
+  // 32 (both halves of the wavefront hold the same 32 scores; s may be past
+  // hi for the padded tail of the range).  DEPTH: key blocks per wavefront
+  // in registers (one scored, the others loading).
+  auto score_range = [&](auto depth, int64_t rb0, int64_t rb1, auto&& sink) {
+    constexpr int kDepth = decltype(depth)::value;
+    // the query row, opaque per call: keeps the q and w loads (96 registers)
+    // inside the call instead of live across a caller's loop
+    int64_t tq = t;
+    asm volatile("" : "+s"(tq));
+    // The key rows and mask entries of blocks [rb0, rb1) are read through
+    // buffer resources based at the first row: the hardware returns 0 for
+    // bytes past the range end (the tail of the last block, never kept), so
+    // a block needs one 32-bit offset and no clamping, and the loads are
+    // unconditional (a load under a branch makes the compiler wait for every
+    // load in flight where the paths join).  Without a mask the mask buffer
+    // is empty: its loads read nothing and give 0.
+    const int64_t row0 = lo + rb0 * KB;
+    int64_t nrows = (rb1 - rb0) * KB;
+    nrows = nrows < hi - row0 ? nrows : hi - row0;
+    nrows = nrows > 0 ? nrows : 0;
+    constexpr int kRowBytes = DT == 3 ? D : 2 * D;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(a.k) + row0 * kRowBytes), (short)0,
+        (int)(nrows * kRowBytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.mask ? a.mask + t * a.mask_ld + row0 : reinterpret_cast<const uint16_t*>(a.w)),
+        (short)0, a.mask ? (int)(nrows * 2) : 0, 0x00020000);
+    constexpr int kNT = 2;  // non-temporal: the keys are read once
+    auto load_mask = [&](int64_t b) -> uint16_t {
+      return __builtin_amdgcn_raw_buffer_load_b16(mrs, (uint32_t)((b - rb0) * KB + m) * 2u, 0, kNT);
     };
-    auto score_blk = [&](int64_t b, const u32x4 (&f)[8], uint16_t mbits) {
-      const int64_t s = lo + b * KB + m;
+    if constexpr (DT != 3) {
+      using M = Mfma<DT>;
+      using T = typename M::T;
+      T A[2][8];
+      float wr[2][16];
+      {
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + tq * H * D;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(stage + swz(4 * i + (lane >> 4), lane & 15)) = f[i];
-      f32x16 acc0, acc1;
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
+          for (int j = 0; j < 8; ++j)
+            A[rb][j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        T bf = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(stage + swz(m, 8 * g + j)));
-        acc0 = M::run(A[0][j], bf, acc0);
-        acc1 = M::run(A[1][j], bf, acc1);
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) wr[rb][jj] = a.w[tq * H + 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3)];
       }
-      const float tot = head_sum(acc0, acc1, wr);
-      emit(b, s, (tot + f16_bits_to_f32(mbits)) + 0.0f);
-    };
 
-    // A ring of kDepth register sets: while a block is scored, the loads of
-    // the next kDepth - 1 blocks of this wave are in flight.
-    if (hi > lo) {
-      u32x4 f[kDepth][8];
-      uint16_t mk[kDepth];
-      const int64_t bs = b0 + wv;
+      // Instruction i of a block load reads bytes [1024 i, 1024 i + 1024) of
+      // the block: lane l gets row 4 i + l / 16, 16-byte chunk l % 16.
+      uint16_t* stage = stage_all + wv * (KB * D);
+      auto load_blk = [&](int64_t b, u32x4 (&f)[8]) {
+        const uint32_t off = (uint32_t)(b - rb0) * (KB * 2 * D) + (uint32_t)lane * 16u;
 #pragma unroll
-      for (int d = 0; d < kDepth - 1; ++d) {
-        const int64_t b = bs + d * NW;
-        mk[d] = 0;
-        if (b < b1) { mk[d] = load_mask(b); load_blk(b, f[d]); }
-      }
-      for (int64_t b = bs; b < b1; b += kDepth * NW) {
+        for (int i = 0; i < 8; ++i)
+          f[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 1024u * i, 0, kNT));
+      };
+      auto score_blk = [&](int64_t b, const u32x4 (&f)[8], uint16_t mbits) {
+        const int64_t s = lo + b * KB + m;
 #pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-          const int64_t bc = b + d * NW;  // scored now, from slot d
-          if (bc >= b1) break;
-          const int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
-          if (bl < b1) { mk[(d + kDepth - 1) % kDepth] = load_mask(bl); load_blk(bl, f[(d + kDepth - 1) % kDepth]); }
-          score_blk(bc, f[d], mk[d]);
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<u32x4*>(stage + swz(4 * i + (lane >> 4), lane & 15)) = f[i];
+        f32x16 acc0, acc1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          T bf = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(stage + swz(m, 8 * g + j)));
+          acc0 = M::run(A[0][j], bf, acc0);
+          acc1 = M::run(A[1][j], bf, acc1);
+        }
+        const float tot = head_sum(acc0, acc1, wr);
+        sink(b, s, (tot + f16_bits_to_f32(mbits)) + 0.0f);
+      };
+
+      // A ring of kDepth register sets: while a block is scored, the loads of
+      // the next kDepth - 1 blocks of this wave are in flight.  Past the end
+      // of the wave's blocks a slot reloads the block being scored (just
+      // read, so cached) and is never scored: every load is unconditional.
+      const int64_t bs = rb0 + wv;
+      if (hi > lo && bs < rb1) {
+        static_assert(kDepth >= 1, "ring depth");
+        u32x4 f[kDepth][8];
+        uint16_t mk[kDepth];
+#pragma unroll
+        for (int d = 0; d < kDepth - 1; ++d) {
+          const int64_t b = bs + d * NW < rb1 ? bs + d * NW : bs;
+          mk[d] = load_mask(b);
+          load_blk(b, f[d]);
+        }
+        for (int64_t b = bs; b < rb1; b += kDepth * NW) {
+#pragma unroll
+          for (int d = 0; d < kDepth; ++d) {
+            const int64_t bc = b + d * NW;  // scored now, from slot d
+            if (bc >= rb1) break;
+            int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
+            bl = bl < rb1 ? bl : bc;
+            mk[(d + kDepth - 1) % kDepth] = load_mask(bl);
+            load_blk(bl, f[(d + kDepth - 1) % kDepth]);
+            score_blk(bc, f[d], mk[d]);
+          }
         }
       }
-    }
-  } else {
-    // FP8 E4M3 q and k with per-row scales (q_scale [n_tok, H], k_scale
-    // [n_kv], positive): S[h,s] = q_scale[t,h] k_scale[s] (q8 . k8), and since
-    // the scales are positive, I = k_scale[s] sum_h (w[t,h] q_scale[t,h])
-    // relu(q8 . k8).  The MFMA k-index maps to the head dimension as
-    // d = 64 (lane / 32) + 32 j + i (j the instruction, i < 32 the byte).
-    // Key rows are 128 bytes: a 32-key block is 4 KiB, and the ring holds
-    // twice as many blocks, so as many bytes are in flight as for f16.
-    using M = Mfma<3>;
-    M::T A[2][2];
-    float wr[2][16];
-    {
-      const unsigned char* qrow = reinterpret_cast<const unsigned char*>(a.q) + t * H * D;
+    } else {
+      // FP8 E4M3 q and k with per-row scales (q_scale [n_tok, H], k_scale
+      // [n_kv], positive): S[h,s] = q_scale[t,h] k_scale[s] (q8 . k8), and
+      // since the scales are positive, I = k_scale[s] sum_h (w[t,h]
+      // q_scale[t,h]) relu(q8 . k8).  The MFMA k-index maps to the head
+      // dimension as d = 64 (lane / 32) + 32 j + i (j the instruction, i < 32
+      // the byte).  Key rows are 128 bytes: a 32-key block is 4 KiB; the q
+      // fragments stay in registers and the ring holds up to four blocks.
+      using M = Mfma<3>;
+      M::T A[2][2];
+      float wr[2][16];
+      {
+        const unsigned char* qrow = reinterpret_cast<const unsigned char*>(a.q) + tq * H * D;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const unsigned char* pq = qrow + (32 * rb + m) * D + 64 * g + 32 * j;
+            const u32x4 lo4 = *reinterpret_cast<const u32x4*>(pq), hi4 = *reinterpret_cast<const u32x4*>(pq + 16);
+            A[rb][j] = M::T{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3], (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+          }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int h = 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3);
+            wr[rb][jj] = a.w[tq * H + h] * a.q_scale[tq * H + h];
+          }
+      }
+      constexpr int kRow8 = D;                  // bytes per key row
+      constexpr int kDepth8 = 2 * (kDepth < 2 ? kDepth : 2);  // (q stays in registers here)
+      unsigned char* stage8 = reinterpret_cast<unsigned char*>(stage_all) + wv * (KB * kRow8);
+      // LDS: 16-byte chunk c of row r at r * 128 + ((c ^ (r & 7)) << 4)
+      auto swz8 = [](int r, int c) { return r * kRow8 + ((c ^ (r & 7)) << 4); };
+      // instruction i of a block load: lane l reads row 8 i + l / 8, chunk l % 8
+      auto load_blk8 = [&](int64_t b, u32x4 (&f)[4]) {
+        const uint32_t off = (uint32_t)(b - rb0) * (KB * kRow8) + (uint32_t)lane * 16u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          f[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 1024u * i, 0, kNT));
+      };
+      auto score_blk8 = [&](int64_t b, const u32x4 (&f)[4], uint16_t mbits) {
+        const int64_t s = lo + b * KB + m;
+        const float ks = a.k_scale[s < last_row ? s : last_row];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(stage8 + swz8(8 * i + (lane >> 3), lane & 7)) = f[i];
+        f32x16 acc0, acc1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const unsigned char* p = qrow + (32 * rb + m) * D + 64 * g + 32 * j;
-          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(p), hi4 = *reinterpret_cast<const u32x4*>(p + 16);
-          A[rb][j] = M::T{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3], (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+          const int c = 4 * g + 2 * j;
+          const u32x4 b0v = *reinterpret_cast<const u32x4*>(stage8 + swz8(m, c));
+          const u32x4 b1v = *reinterpret_cast<const u32x4*>(stage8 + swz8(m, c + 1));
+          const M::T bf = {(int)b0v[0], (int)b0v[1], (int)b0v[2], (int)b0v[3], (int)b1v[0], (int)b1v[1], (int)b1v[2], (int)b1v[3]};
+          acc0 = M::run(A[0][j], bf, acc0);
+          acc1 = M::run(A[1][j], bf, acc1);
         }
+        const float tot = head_sum(acc0, acc1, wr);
+        sink(b, s, (tot * ks + f16_bits_to_f32(mbits)) + 0.0f);
+      };
+      const int64_t bs = rb0 + wv;
+      if (hi > lo && bs < rb1) {
+        u32x4 f[kDepth8][4];
+        uint16_t mk[kDepth8];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int h = 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3);
-          wr[rb][jj] = a.w[t * H + h] * a.q_scale[t * H + h];
+        for (int d = 0; d < kDepth8 - 1; ++d) {
+          const int64_t b = bs + d * NW < rb1 ? bs + d * NW : bs;
+          mk[d] = load_mask(b);
+          load_blk8(b, f[d]);
         }
+        for (int64_t b = bs; b < rb1; b += kDepth8 * NW) {
+#pragma unroll
+          for (int d = 0; d < kDepth8; ++d) {
+            const int64_t bc = b + d * NW;
+            if (bc >= rb1) break;
+            int64_t bl = bc + (kDepth8 - 1) * NW;
+            bl = bl < rb1 ? bl : bc;
+            mk[(d + kDepth8 - 1) % kDepth8] = load_mask(bl);
+            load_blk8(bl, f[(d + kDepth8 - 1) % kDepth8]);
+            score_blk8(bc, f[d], mk[d]);
+          }
+        }
+      }
     }
-    constexpr int kRow8 = D;                  // bytes per key row
-    constexpr int kDepth8 = 2 * kDepth;
-    const unsigned char* kb8 = reinterpret_cast<const unsigned char*>(a.k);
-    unsigned char* stage8 = reinterpret_cast<unsigned char*>(stage_all) + wv * (KB * kRow8);
-    // LDS: 16-byte chunk c of row r at r * 128 + ((c ^ (r & 7)) << 4)
-    auto swz8 = [](int r, int c) { return r * kRow8 + ((c ^ (r & 7)) << 4); };
-    // instruction i of a block load: lane l reads row 8 i + l / 8, chunk l % 8
-    auto load_blk8 = [&](int64_t b, u32x4 (&f)[4]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t s = lo + b * KB + 8 * i + (lane >> 3);
-        s = s < last_row ? s : last_row;
-        f[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb8 + s * kRow8 + (lane & 7) * 16));
-      }
-    };
-    auto score_blk8 = [&](int64_t b, const u32x4 (&f)[4], uint16_t mbits) {
-      const int64_t s = lo + b * KB + m;
-      const float ks = a.k_scale[s < last_row ? s : last_row];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(stage8 + swz8(8 * i + (lane >> 3), lane & 7)) = f[i];
-      f32x16 acc0, acc1;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { acc0[e] = 0.f; acc1[e] = 0.f; }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = 4 * g + 2 * j;
-        const u32x4 b0v = *reinterpret_cast<const u32x4*>(stage8 + swz8(m, c));
-        const u32x4 b1v = *reinterpret_cast<const u32x4*>(stage8 + swz8(m, c + 1));
-        const M::T bf = {(int)b0v[0], (int)b0v[1], (int)b0v[2], (int)b0v[3], (int)b1v[0], (int)b1v[1], (int)b1v[2], (int)b1v[3]};
-        acc0 = M::run(A[0][j], bf, acc0);
-        acc1 = M::run(A[1][j], bf, acc1);
-      }
-      const float tot = head_sum(acc0, acc1, wr);
-      emit(b, s, (tot * ks + f16_bits_to_f32(mbits)) + 0.0f);
-    };
-    if (hi > lo) {
-      u32x4 f[kDepth8][4];
-      uint16_t mk[kDepth8];
-      const int64_t bs = b0 + wv;
-#pragma unroll
-      for (int d = 0; d < kDepth8 - 1; ++d) {
-        const int64_t b = bs + d * NW;
-        mk[d] = 0;
-        if (b < b1) { mk[d] = load_mask(b); load_blk8(b, f[d]); }
-      }
-      for (int64_t b = bs; b < b1; b += kDepth8 * NW) {
-#pragma unroll
-        for (int d = 0; d < kDepth8; ++d) {
-          const int64_t bc = b + d * NW;
-          if (bc >= b1) break;
-          const int64_t bl = bc + (kDepth8 - 1) * NW;
-          if (bl < b1) { mk[(d + kDepth8 - 1) % kDepth8] = load_mask(bl); load_blk8(bl, f[(d + kDepth8 - 1) % kDepth8]); }
-          score_blk8(bc, f[d], mk[d]);
-        }
+  };
+  auto valid_key = [&](int64_t s, float v) -> uint64_t {
+    return (s < hi && v != -__builtin_inff()) ? make_key(v, (uint32_t)s) : 0ull;
+  };
+
+  if constexpr (FORM == kFormRaw) {
+    uint32_t* raw = a.raw + (size_t)t * a.raw_ld;
+    score_range(std::integral_constant<int, kRingDepth>{}, b0, b1, [&](int64_t b, int64_t s, float v) {
+      if (g == 0)
+        __hip_atomic_store(&raw[b * KB + m], (s < hi && v != -__builtin_inff()) ? ord_f32(v) : 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    });
+  } else if constexpr (FORM == kFormLists) {
+    score_range(std::integral_constant<int, kRingDepth>{}, b0, b1, [&](int64_t b, int64_t s, float v) {
+      if (g == 0) arr[(b - b0) * KB + m] = valid_key(s, v);
+    });
+  } else {
+    // every wavefront keeps its best kTopsC keys while it streams; the
+    // workgroup's summary is the best kTopsC of the wavefronts' ones
+    const TopsLds L = tops_lds(keys_per_wg, P);
+    uint64_t* tw = reinterpret_cast<uint64_t*>(smem + L.arr);  // [NW][kTopsC], then [NW][kTopsBuf]
+    TopsState st{0ull, 0ull, 0, tw + NW * kTopsC + wv * kTopsBuf};
+    score_range(std::integral_constant<int, kRingDepth>{}, b0, b1,
+                [&](int64_t b, int64_t s, float v) { tops_insert(st, valid_key(s, v), lane); });
+    if (st.nbuf) tops_flush(st, lane);
+    if (lane < kTopsC) tw[wv * kTopsC + lane] = st.top;
+    __syncthreads();
+    if (wv == 0) {
+      uint64_t x[2] = {tw[2 * lane], tw[2 * lane + 1]};
+      wave_sort_reg<2>(x, lane);
+      uint64_t* out = a.lists + ((size_t)t * P + p) * kTopsC;
+      if (lane < kTopsC / 2) {
+        __hip_atomic_store(&out[2 * lane], x[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&out[2 * lane + 1], x[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   __syncthreads();
 
-  if (!RAW) {
+  if constexpr (FORM == kFormLists) {
     // the stage buffers are free now: histograms and reduction slots
     uint32_t* shw = reinterpret_cast<uint32_t*>(smem);
     uint32_t* sred = reinterpret_cast<uint32_t*>(smem + kSelHistBytes);
@@ -604,37 +741,125 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   // and loads (coherent across the XCDs' separate L2 caches without writing
   // back or invalidating them, which device-scope fences would do); every
   // store has completed (vmcnt(0)) before the counter moves.
+  uint32_t* s_flag = s_last;
+  if constexpr (FORM == kFormTops) s_flag = reinterpret_cast<uint32_t*>(smem + tops_lds(keys_per_wg, P).ints);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
-    s_last[0] = __builtin_amdgcn_atomic_inc32(a.counters + t, (unsigned)(P - 1), __ATOMIC_RELAXED, "agent") ==
+    s_flag[0] = __builtin_amdgcn_atomic_inc32(a.counters + t, (unsigned)(P - 1), __ATOMIC_RELAXED, "agent") ==
                         (unsigned)(P - 1) ? 1u : 0u;
   __syncthreads();
-  if (!s_last[0]) return;
-  if (RAW)
+  if (!s_flag[0]) return;
+  if constexpr (FORM == kFormRaw) {
     select_raw(a, t, (int)(nblk * KB), lo, smem);
-  else
+  } else if constexpr (FORM == kFormLists) {
     finish_lists(a, ch, t, smem);
+  } else {
+    // The K best of the query from the P summaries (each the sorted kTopsC
+    // best keys of one split).  The merge tree gives the K best candidates,
+    // whose K-th key tau bounds the answer from below.  A split whose
+    // kTopsC-th key is above tau may hold further keys above tau: the
+    // one with the highest such key is scored again into LDS, its K best
+    // replace its summary among the candidates, and the tree runs again,
+    // until no summary is cut short above tau (every key of the answer is
+    // then a candidate).  Each split is re-scored at most once.
+    const int K = a.K;
+    const TopsLds L = tops_lds(keys_per_wg, P);
+    uint64_t* cand = reinterpret_cast<uint64_t*>(smem);               // [4096] (stage region)
+    uint64_t* alt = cand + 4096;                                       // [2048]
+    uint64_t* ex = reinterpret_cast<uint64_t*>(smem + L.arr);          // [keys_per_wg] a re-scored split
+    uint64_t* best = reinterpret_cast<uint64_t*>(smem + L.best);       // [kTreeCap]
+    BlockShared* shs = reinterpret_cast<BlockShared*>(smem + L.sh);
+    uint32_t* red = reinterpret_cast<uint32_t*>(smem + L.red);
+    uint64_t* lastc = reinterpret_cast<uint64_t*>(smem + L.lastc);     // [P] kTopsC-th key per summary
+    uint8_t* done = smem + L.flags;                                    // [P] split re-scored
+    unsigned long long* s_emax = reinterpret_cast<unsigned long long*>(smem + L.ints + 8);
+    int* s_pick = reinterpret_cast<int*>(smem + L.ints + 16);
+    const uint64_t* sums = a.lists + (size_t)t * P * kTopsC;
+    const int m0 = P * kTopsC;  // <= 4096 (host-checked)
+    for (int i = tid; i < m0; i += BS) {
+      const uint64_t key = __hip_atomic_load(&sums[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      cand[i] = key;
+      if (i % kTopsC == kTopsC - 1) lastc[i / kTopsC] = key;
+    }
+    for (int i = tid; i < P; i += BS) done[i] = 0;
+    if (tid == 0) *s_emax = 0ull;
+    __syncthreads();
+    int mc = m0;
+    for (;;) {
+      if (mc > 4 * kTreeCap) {
+        // more than 2048 candidates: a radix select cuts them to the K best
+        // first (fewer vector instructions than sorting them all; measured
+        // slower at 2048 and below), and the tree then only sorts those
+        const int ns = block_select_compact_reg<kDecodeTopsMax / BS>(cand, mc, K, alt, nullptr, shs, red);
+        block_topk_tree_any(alt, cand, ns, K, nullptr, nullptr, best);
+      } else {
+        block_topk_tree_any(cand, alt, mc, K, nullptr, nullptr, best);
+      }
+      const uint64_t tau = best[K - 1];
+      uint64_t e = 0ull;
+      for (int i = tid; i < P; i += BS)
+        if (!done[i] && lastc[i] > tau && lastc[i] > e) e = lastc[i];
+      e = wave_reduce_u64(e, [](uint64_t x, uint64_t y) { return x > y ? x : y; });
+      if (lane == 0 && e) atomicMax(s_emax, (unsigned long long)e);
+      __syncthreads();
+      const uint64_t emax = *s_emax;
+      if (emax == 0ull) break;
+      for (int i = tid; i < P; i += BS)
+        if (!done[i] && lastc[i] == emax) *s_pick = i;
+      __syncthreads();
+      const int pe = *s_pick;
+      if (tid == 0) { done[pe] = 1; *s_emax = 0ull; }
+      const int64_t eb0 = nblk * pe / P, eb1 = nblk * (pe + 1) / P;
+      const int64_t slo = lo + eb0 * KB, shi = lo + eb1 * KB;  // the split's keys
+      score_range(std::integral_constant<int, 1>{}, eb0, eb1, [&](int64_t b, int64_t s, float v) {
+        if (g == 0) ex[(b - eb0) * KB + m] = valid_key(s, v);
+      });
+      __syncthreads();
+      // the other splits' keys among the K best, then the split's own K best
+      const uint64_t bk = tid < K ? best[tid] : 0ull;
+      const int64_t bs = (int64_t)key_index(bk);
+      const bool keep = bk != 0ull && (bs < slo || bs >= shi);
+      int nb;
+      const int pos = block_excl_scan(keep ? 1 : 0, &nb, *shs);
+      if (keep) cand[pos] = bk;
+      const int ns = block_select_compact_any(ex, (int)((eb1 - eb0) * KB), K, cand + nb, nullptr, shs, red);
+      mc = nb + ns;
+    }
+    for (int i = tid; i < K; i += BS) {
+      a.idx[t * K + i] = key_index(best[i]);
+      if (a.score) a.score[t * K + i] = key_score(best[i]);
+    }
+  }
 }
 
-template <int DT, bool RAW>
+template <int DT, int FORM>
 hipError_t launch_one(const KArgs& a, int keys_per_wg, int ch, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DT, RAW>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DT, FORM>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)(a.n_tok * a.P));
-  hipLaunchKernelGGL((decode_kernel<DT, RAW>), grid, dim3(BS), decode_lds_bytes(keys_per_wg, a.K, a.P, ch, RAW), st,
+  hipLaunchKernelGGL((decode_kernel<DT, FORM>), grid, dim3(BS), decode_lds_bytes(keys_per_wg, a.K, a.P, ch, FORM), st,
                      a, keys_per_wg, ch);
   return hipGetLastError();
 }
 
+template <int DT>
+hipError_t launch_dt(const KArgs& a, int keys_per_wg, int ch, int form, hipStream_t st) {
+  if (form == kFormRaw) return launch_one<DT, kFormRaw>(a, keys_per_wg, ch, st);
+  if (form == kFormTops) return launch_one<DT, kFormTops>(a, keys_per_wg, ch, st);
+  return launch_one<DT, kFormLists>(a, keys_per_wg, ch, st);
+}
+
 }  // namespace
 
-size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw) {
+size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form) {
+  if (form == kFormTops) return tops_lds(keys_per_wg, P).total;
+  const bool raw = form == kFormRaw;
   const size_t scoring = (size_t)kStageBytes + (size_t)keys_per_wg * 8 + (size_t)next_pow2(K) * 8 + 2 * BS * 8 +
                          sizeof(BlockShared) + 16;
   size_t finish;
@@ -646,10 +871,10 @@ size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw) {
   return scoring > finish ? scoring : finish;
 }
 
-hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, bool raw, hipStream_t st) {
-  if (a.dtype == 1) return raw ? launch_one<1, true>(a, keys_per_wg, ch, st) : launch_one<1, false>(a, keys_per_wg, ch, st);
-  if (a.dtype == 3) return raw ? launch_one<3, true>(a, keys_per_wg, ch, st) : launch_one<3, false>(a, keys_per_wg, ch, st);
-  return raw ? launch_one<2, true>(a, keys_per_wg, ch, st) : launch_one<2, false>(a, keys_per_wg, ch, st);
+hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, int form, hipStream_t st) {
+  if (a.dtype == 1) return launch_dt<1>(a, keys_per_wg, ch, form, st);
+  if (a.dtype == 3) return launch_dt<3>(a, keys_per_wg, ch, form, st);
+  return launch_dt<2>(a, keys_per_wg, ch, form, st);
 }
 
 }  // namespace lid

@@ -19,6 +19,7 @@ constexpr int kDecodeKeysPerSplit = 256;
 constexpr int64_t kCUs = 256;          // MI355X compute units
 constexpr int kDecodeMaxSplits = 256;  // bounds the decode workspace independently of n_kv
 constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kTreeCapHost = 512;     // k_top range of the decode merge tree: next_pow2(k_top) == 512
 
 struct Plan {
   int kind;         // lid_plan (never AUTO)
@@ -27,7 +28,9 @@ struct Plan {
   int cap;          // per-wave candidate capacity
   int keys_per_wg;  // decode: LDS key slots per workgroup
   int ch;           // merge: entries per list per round
-  bool raw;         // decode: raw-score form (the last workgroup selects from all scores)
+  int form;         // decode finish: 0 sorted split lists, 1 raw scores (the last workgroup
+                    // selects from all of them), 2 split summaries (the best kDecodeTopsC keys
+                    // of every split; a split is scored again if its summary is too short)
   int fuse;         // prefill, P > 1: the scoring kernel finishes from the split lists itself
                     // (1: merging sorted lists, 2: selecting from unsorted ones)
   int64_t raw_ld;   // decode, raw form: scores per query row
@@ -134,15 +137,22 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (kp > kDecodeMaxKeys) return LID_ERR_UNSUPPORTED;
     pl->keys_per_wg = (int)kp;
     const int64_t span = cdiv(s->n_kv, 32) * 32;  // longest visible range, in 32-key blocks
-    pl->raw = span <= kRawMax;
-    if (P > 1) pl->ch = merge_chunk(P, K);
-    if (decode_lds_bytes(pl->keys_per_wg, K, P, pl->ch, pl->raw) > kMaxLds) return LID_ERR_UNSUPPORTED;
+    // summaries when the merge tree applies and P kDecodeTopsC holds about 4 K
+    // keys (then a split rarely holds more than kDecodeTopsC of the answer);
+    // else raw scores for short ranges, sorted split lists for long ones
+    const bool tops = P >= 2 && next_pow2(K) == kTreeCapHost && (int64_t)P * kDecodeTopsC <= kDecodeTopsMax &&
+                      (int64_t)P * kDecodeTopsC >= 4LL * K;
+    pl->form = tops ? 2 : (span <= kRawMax ? 1 : 0);
+    if (P > 1 && pl->form == 0) pl->ch = merge_chunk(P, K);
+    if (decode_lds_bytes(pl->keys_per_wg, K, P, pl->ch, pl->form) > kMaxLds) return LID_ERR_UNSUPPORTED;
     // workspace: per-query counters (zero between launches), then the raw
-    // scores or the per-split lists
+    // scores, the per-split lists or the summaries
     pl->ws_data = (size_t)cdiv(s->n_tok * 4, 256) * 256;
-    if (pl->raw) {
+    if (pl->form == 1) {
       pl->raw_ld = cdiv(span, 64) * 64;
       pl->ws = pl->ws_data + (size_t)s->n_tok * pl->raw_ld * sizeof(uint32_t);
+    } else if (pl->form == 2) {
+      pl->ws = pl->ws_data + (size_t)s->n_tok * P * kDecodeTopsC * sizeof(uint64_t);
     } else {
       pl->ws = pl->ws_data + (P > 1 ? (size_t)s->n_tok * P * K * sizeof(uint64_t) : 0);
     }
@@ -233,7 +243,7 @@ int topk_impl(const lid_shape* shape, const void* q, const float* q_scale, const
   hipError_t e;
   if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
   if (pl.kind == LID_PLAN_PREFILL) e = launch_prefill(a, pl.nw, st);
-  else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, pl.ch, pl.raw, st);
+  else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, pl.ch, pl.form, st);
   else e = launch_generic(a, st);
   if (e != hipSuccess) return hip_fail(e);
   if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);

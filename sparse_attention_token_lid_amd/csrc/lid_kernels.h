@@ -17,7 +17,8 @@ struct KArgs {
   const int32_t* kv_range;  // [n_tok, 2], or null
   int32_t* idx;             // [n_tok, K]
   float* score;             // [n_tok, K], or null
-  uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1)
+  uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1); decode tops
+                            // form: [n_tok, P, kDecodeTopsC] split summaries
   uint32_t* raw;            // decode, raw form: [n_tok, raw_ld] ordered scores (0 = no key)
   float* scores;            // score-only mode: [n_tok, scores_ld] f32 output
   int64_t scores_ld;
@@ -38,6 +39,8 @@ constexpr int kMfmaDim = 128;
 constexpr int kPrefillTile = 128;      // keys per LDS tile
 constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
 constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
+constexpr int kDecodeTopsC = 16;       // decode, tops form: keys in each split's summary
+constexpr int kDecodeTopsMax = 4096;   // decode, tops form: most summary keys per query (P kDecodeTopsC)
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
 constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <= 64 x this keys
 
@@ -48,8 +51,9 @@ hipError_t launch_scores_fill(const KArgs& a, hipStream_t st);     // -inf outsi
 hipError_t launch_generic_scores(const KArgs& a, hipStream_t st);  // score-only mode, any shape
 size_t prefill_lds_bytes(int nw, int cap);
 
-hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, bool raw, hipStream_t st);
-size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, bool raw);
+// decode finish forms: 0 sorted split lists, 1 raw scores, 2 split summaries
+hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, int form, hipStream_t st);
+size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form);
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st);
 size_t merge_lds_bytes(int P, int K, int ch);
