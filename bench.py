@@ -46,16 +46,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources; a stored traffic figure is only reported
-    while the kernels it was measured on are unchanged."""
+# the sources each plan's scoring kernel is compiled from
+PLAN_SOURCES = {
+    "decode": ["k_decode.hip", "lid_device.h", "lid_kernels.h", "lid_merge.h", "lid_select.h"],
+    "prefill": ["k_prefill.hip", "lid_device.h", "lid_kernels.h"],
+    "generic": ["k_generic.hip", "lid_device.h", "lid_kernels.h"],
+}
+
+
+def kernel_source_hash(plan: str = None) -> str:
+    """sha256 over the HIP sources of a plan's scoring kernel (all sources
+    when plan is None); a stored traffic figure is only reported while the
+    kernel it was measured on is unchanged."""
     import hashlib
     csrc = os.path.join(ROOT, "sparse_attention_token_lid_amd", "csrc")
+    names = PLAN_SOURCES.get(plan) or [n for n in os.listdir(csrc) if n.endswith((".hip", ".h"))]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in sorted(names):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -67,7 +76,7 @@ def stored_traffic(workload: str, plan: str, splits: int):
         rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(plan):
         return None
     if rec.get("plan") != plan or rec.get("splits") != splits:
         return None
@@ -368,7 +377,7 @@ def main():
         "timing": "HIP-graph replay of the timed steps",
         "eager_ms_per_step": eager_ms_per_step,
         "scoring_kernel_us": kern_ms * 1e3,
-        "kernel_hash": kernel_source_hash(),
+        "kernel_hash": kernel_source_hash(plan),
         "roofline": roof,
     }
     if not args.no_cpu_baseline and not scores_mode and not fp8:

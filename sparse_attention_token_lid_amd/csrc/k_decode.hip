@@ -499,10 +499,12 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     asm volatile("" : "+s"(tq));
     // The key rows and mask entries of blocks [rb0, rb1) are read through
     // buffer resources based at the first row: the hardware returns 0 for
-    // bytes past the range end (the tail of the last block, never kept), so
+    // bytes past the range end (the tail of the last block, and the ring's
+    // look-ahead past the last block; never kept) without reading memory, so
     // a block needs one 32-bit offset and no clamping, and the loads are
     // unconditional (a load under a branch makes the compiler wait for every
-    // load in flight where the paths join).  Without a mask the mask buffer
+    // load in flight where the paths join).  Offsets stay below 2^22: at most
+    // kDecodeMaxKeys + 32 (NW kDepth) rows.  Without a mask the mask buffer
     // is empty: its loads read nothing and give 0.
     const int64_t row0 = lo + rb0 * KB;
     int64_t nrows = (rb1 - rb0) * KB;
@@ -566,8 +568,9 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
 
       // A ring of kDepth register sets: while a block is scored, the loads of
       // the next kDepth - 1 blocks of this wave are in flight.  Past the end
-      // of the wave's blocks a slot reloads the block being scored (just
-      // read, so cached) and is never scored: every load is unconditional.
+      // of the wave's blocks a slot loads from beyond the buffer's range
+      // (zeros, no memory access) and is never scored: every load is
+      // unconditional.
       const int64_t bs = rb0 + wv;
       if (hi > lo && bs < rb1) {
         static_assert(kDepth >= 1, "ring depth");
@@ -575,17 +578,15 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
         uint16_t mk[kDepth];
 #pragma unroll
         for (int d = 0; d < kDepth - 1; ++d) {
-          const int64_t b = bs + d * NW < rb1 ? bs + d * NW : bs;
-          mk[d] = load_mask(b);
-          load_blk(b, f[d]);
+          mk[d] = load_mask(bs + d * NW);
+          load_blk(bs + d * NW, f[d]);
         }
         for (int64_t b = bs; b < rb1; b += kDepth * NW) {
 #pragma unroll
           for (int d = 0; d < kDepth; ++d) {
             const int64_t bc = b + d * NW;  // scored now, from slot d
             if (bc >= rb1) break;
-            int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
-            bl = bl < rb1 ? bl : bc;
+            const int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
             mk[(d + kDepth - 1) % kDepth] = load_mask(bl);
             load_blk(bl, f[(d + kDepth - 1) % kDepth]);
             score_blk(bc, f[d], mk[d]);
@@ -659,17 +660,15 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
         uint16_t mk[kDepth8];
 #pragma unroll
         for (int d = 0; d < kDepth8 - 1; ++d) {
-          const int64_t b = bs + d * NW < rb1 ? bs + d * NW : bs;
-          mk[d] = load_mask(b);
-          load_blk8(b, f[d]);
+          mk[d] = load_mask(bs + d * NW);
+          load_blk8(bs + d * NW, f[d]);
         }
         for (int64_t b = bs; b < rb1; b += kDepth8 * NW) {
 #pragma unroll
           for (int d = 0; d < kDepth8; ++d) {
             const int64_t bc = b + d * NW;
             if (bc >= rb1) break;
-            int64_t bl = bc + (kDepth8 - 1) * NW;
-            bl = bl < rb1 ? bl : bc;
+            const int64_t bl = bc + (kDepth8 - 1) * NW;
             mk[(d + kDepth8 - 1) % kDepth8] = load_mask(bl);
             load_blk8(bl, f[(d + kDepth8 - 1) % kDepth8]);
             score_blk8(bc, f[d], mk[d]);
