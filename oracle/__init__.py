@@ -9,7 +9,9 @@ Parity pins (tests/test_oracle*.py): a hand-worked golden example, the H=1/D=1
 closed form (a plain sort), the q=0 tie case, exhaustive f16/bf16 decode
 against numpy, rank-count brute force on tiny inputs, and the invariants
 (masked keys never chosen, <=k_top visible keys all returned, selected >=
-unselected, key permutation, inert w=0 head, linearity in w).
+unselected, key permutation, inert w=0 head, linearity in w).  The shared
+(per-ubatch) top-k is pinned by its one-query case (the per-query top-k), a
+numpy brute force, identical queries (U = n_tok v) and the -inf rule.
 """
 from __future__ import annotations
 
@@ -56,6 +58,8 @@ def load_library(path: str):
     lib.lid_oracle_topk_scaled.restype = ctypes.c_int
     lib.lid_oracle_topk_scaled.argtypes = [i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp,
                                            vp, vp, vp, i32]
+    lib.lid_oracle_topk_shared.restype = ctypes.c_int
+    lib.lid_oracle_topk_shared.argtypes = [i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, vp, vp, i32]
     lib.lid_oracle_scores_scaled.restype = ctypes.c_int
     lib.lid_oracle_scores_scaled.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, i32]
     lib.lid_oracle_f8e4m3_to_f64.restype = ctypes.c_double
@@ -88,6 +92,9 @@ class Oracle:
 
     def scores(self, *a, **kw):
         return scores(*a, _lib=self._lib, **kw)
+
+    def topk_shared(self, *a, **kw):
+        return topk_shared(*a, _lib=self._lib, **kw)
 
     def f16_to_f64(self, bits):
         return self._lib.lid_oracle_f16_to_f64(bits)
@@ -189,6 +196,26 @@ def scores(q, k, w, mask=None, kv_range=None, qk_dtype=None, rows=None, threads=
     if rc != 0:
         raise RuntimeError(f"lid_oracle_scores failed: {rc}")
     return v
+
+
+def topk_shared(q, k, w, mask=None, kv_range=None, k_top=512, qk_dtype=None, threads=0, _lib=None):
+    """Oracle shared (per-ubatch) top-k: the k_top keys with the largest
+    U[s] = sum_t v[t,s] over all queries.  Returns (idx int32 [k_top],
+    score f32 [k_top], maxabs = max |U| over the selectable keys)."""
+    q, k, w, mask, kv_range, dt = _prep(q, k, w, mask, kv_range, qk_dtype, None)
+    n_tok, H, D = q.shape
+    n_kv = k.shape[0]
+    idx = np.empty(k_top, dtype=np.int32)
+    score = np.empty(k_top, dtype=np.float32)
+    maxabs = ctypes.c_double(0.0)
+    mask_ld = 0 if mask is None else mask.shape[1]
+    lib = _lib or _load()
+    rc = lib.lid_oracle_topk_shared(n_tok, n_kv, H, D, k_top, DTYPE_CODE[dt], _ptr(q), _ptr(k), _ptr(w),
+                                    _ptr(mask), mask_ld, _ptr(kv_range), _ptr(idx), _ptr(score),
+                                    ctypes.addressof(maxabs), threads)
+    if rc != 0:
+        raise RuntimeError(f"lid_oracle_topk_shared failed: {rc}")
+    return idx, score, maxabs.value
 
 
 def f16_to_f64(bits: int) -> float:

@@ -357,3 +357,89 @@ int lid_oracle_scores_scaled(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, 
     return scores_impl(n_tok, n_kv, H, D, dtype, q, k, w, mask, mask_ld, kv_range, v_out, n_threads,
                        q_scale, k_scale);
 }
+
+/*
+ * Shared (per-ubatch) top-k: one selection for all the queries of a ubatch.
+ * ggml-org llama.cpp PR 22378, the batched-prefill commit: the indexer's
+ * per-query scores are summed over the ubatch's queries (and heads) and a
+ * single ubatch-wide top-k is taken, which every query then uses; the later
+ * commit that reverts collapse-Q writes this summed form as
+ * top_k(sum_q relu(kv * q) * w).  Written out:
+ *     U[s] = sum_t v[t,s]
+ * where v[t,s] is the masked f32 score of steps 1-3 (the value the per-query
+ * top-k selects from), and a term of -inf (key outside query t's range, or
+ * masked for it) makes U[s] = -inf: the key is not selectable.  The terms are
+ * summed in double, U is rounded to f32 once, and the k_top keys with the
+ * largest U are returned, ordered by U descending and, on equal U, by index
+ * ascending (the per-query conventions of step 4).  A ubatch without queries
+ * sums nothing: U = 0 for every key.
+ *   idx_out [k_top] int32, score_out [k_top] f32 (may be NULL),
+ *   maxabs_out: max |U[s]| over the selectable keys (may be NULL).
+ */
+int lid_oracle_topk_shared(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, int32_t k_top,
+                           int32_t dtype, const void* q, const void* k, const float* w,
+                           const uint16_t* mask, int64_t mask_ld, const int32_t* kv_range,
+                           int32_t* idx_out, float* score_out, double* maxabs_out,
+                           int32_t n_threads)
+{
+    int rc = check_args(n_tok, n_kv, H, D, dtype, q, k, w, mask_ld, mask);
+    if (rc) return rc;
+    if (k_top <= 0 || !idx_out) return ORC_EINVAL;
+    double* kd = decode_keys(k, dtype, n_kv, D, NULL);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1) * (size_t)H * (size_t)D);
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1) * (size_t)H);
+    cand* c = (cand*)malloc(sizeof(cand) * (size_t)(n_kv > 0 ? n_kv : 1));
+    int64_t* lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_tok > 0 ? n_tok : 1));
+    int64_t* hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_tok > 0 ? n_tok : 1));
+    uint8_t* ok = (uint8_t*)malloc((size_t)(n_kv > 0 ? n_kv : 1));
+    if (!kd || !qd || !wd || !c || !lo || !hi || !ok) {
+        free(kd); free(qd); free(wd); free(c); free(lo); free(hi); free(ok);
+        return ORC_ENOMEM;
+    }
+    for (int64_t i = 0; i < n_tok * H * D; ++i)
+        qd[i] = decode(q, dtype, i);
+    for (int64_t i = 0; i < n_tok * H; ++i)
+        wd[i] = (double)w[i];
+    for (int64_t t = 0; t < n_tok; ++t)
+        key_range(kv_range, t, n_kv, &lo[t], &hi[t]);
+
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 64) reduction(min : err)
+    for (int64_t s = 0; s < n_kv; ++s) {
+        double U = 0.0;
+        int selectable = 1;
+        for (int64_t t = 0; t < n_tok && selectable; ++t) {
+            if (s < lo[t] || s >= hi[t]) { selectable = 0; break; }   /* v = -inf */
+            double I = head_reduced_score(qd + t * H * D, wd + t * H, kd + s * D, H, D);
+            float v;
+            if (masked_score(I, mask, mask_ld, t, s, &v)) { err = ORC_ENONFINITE; selectable = 0; break; }
+            if (isinf(v)) { selectable = 0; break; }                 /* -inf term */
+            U += (double)v;
+        }
+        ok[s] = (uint8_t)selectable;
+        c[s].v = (float)U + 0.0f;
+        c[s].s = s;
+    }
+    double maxabs = 0.0;
+    int64_t n = 0;
+    for (int64_t s = 0; s < n_kv; ++s) {
+        if (!ok[s]) continue;
+        if (fabs((double)c[s].v) > maxabs) maxabs = fabs((double)c[s].v);
+        c[n++] = c[s];
+    }
+    qsort(c, (size_t)n, sizeof(cand), cand_cmp);
+    for (int32_t j = 0; j < k_top; ++j) {
+        int valid = j < n;
+        idx_out[j] = valid ? (int32_t)c[j].s : -1;
+        if (score_out)
+            score_out[j] = valid ? c[j].v : -INFINITY;
+    }
+    free(kd); free(qd); free(wd); free(c); free(lo); free(hi); free(ok);
+    if (maxabs_out) *maxabs_out = maxabs;
+    return err;
+}

@@ -370,3 +370,89 @@ def test_mask_and_ranges_forms_agree(oracle_lib):
     a = oracle_lib.topk(d["q"], d["k"], d["w"], mask=d["mask"], k_top=16)
     b = oracle_lib.topk(d["q"], d["k"], d["w"], kv_range=d["ranges"], k_top=16)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- shared (per-ubatch) top-k
+
+def _shared_rank_select(v, k_top):
+    """Brute force of the shared top-k from exact per-query scores v [n_tok,
+    n_kv]: U[s] = sum_t v[t,s] as an exact rational (any -inf term excludes
+    the key), rounded to f32 once, then selection by rank counting."""
+    n_tok, n_kv = v.shape
+    U = np.full(n_kv, -np.inf)
+    for s in range(n_kv):
+        if np.all(v[:, s] != -np.inf):
+            U[s] = np.float32(float(sum((Fraction(float(x)) for x in v[:, s]), Fraction(0)))) + np.float32(0.0)
+    return _rank_select(U, k_top)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_shared_bruteforce_exact(oracle_lib, seed):
+    """Small-integer inputs with masks and ranges: the shared top-k equals the
+    exact brute force bit for bit (ties by index included)."""
+    rng = np.random.default_rng(100 + seed)
+    n_tok, n_kv, H, D = 4, int(rng.integers(20, 60)), int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    k_top = int(rng.integers(1, 25))
+    q = rng.integers(-2, 3, (n_tok, H, D)).astype(np.float16)
+    k = rng.integers(-2, 3, (n_kv, D)).astype(np.float16)
+    w = rng.choice(np.array([0, 0.25, 0.5, 1, -0.5, 2], np.float32), (n_tok, H))
+    mask = rng.choice(np.array([0, 0, 0, 0, -0.5, 1, -np.inf], np.float16), (n_tok, n_kv))
+    ranges = np.array([[0, n_kv], [2, n_kv], [0, n_kv - 3], [1, n_kv - 1]], np.int32)
+    use_mask, use_ranges = seed % 2 == 0, seed >= 2
+    v = _exact_scores(q, k, w, mask if use_mask else None, ranges if use_ranges else None)
+    idx, sc, _ = oracle_lib.topk_shared(q, k, w, mask=mask if use_mask else None,
+                                        kv_range=ranges if use_ranges else None, k_top=k_top)
+    ei, es = _shared_rank_select(v, k_top)
+    assert idx.tolist() == ei
+    assert sc.tolist() == es
+
+
+def test_shared_bruteforce_random(oracle_lib):
+    """Random normal f16 inputs: scores agree with the exact brute force to
+    f32 rounding and the index sets agree."""
+    q, k, w = li.draw_qkw(3, 80, 4, 8, "f16", True, seed=11)
+    v = _exact_scores(q, k, w, None, None)
+    idx, sc, _ = oracle_lib.topk_shared(q, k, w, k_top=17)
+    ei, es = _shared_rank_select(v, 17)
+    assert idx.tolist() == ei
+    np.testing.assert_allclose(sc, es, rtol=2e-7, atol=0)
+
+
+def test_shared_one_query_is_per_query_topk(oracle_lib):
+    """A ubatch of one query: U = v, so the shared top-k is that query's top-k."""
+    d = li.make("c1", seed=5)
+    for t in range(d["q"].shape[0]):
+        sl = slice(t, t + 1)
+        i1, s1, _ = oracle_lib.topk(d["q"][sl], d["k"], d["w"][sl], mask=d["mask"][sl], k_top=16)
+        i2, s2, _ = oracle_lib.topk_shared(d["q"][sl], d["k"], d["w"][sl], mask=d["mask"][sl], k_top=16)
+        assert i2.tolist() == i1[0].tolist() and s2.tolist() == s1[0].tolist()
+
+
+def test_shared_identical_queries_scale(oracle_lib):
+    """Four copies of one query (no mask): U = 4 v exactly, so the shared
+    top-k has the query's own indices and four times its scores."""
+    q, k, w = li.draw_qkw(1, 200, 4, 16, "f16", True, seed=12)
+    i1, s1, _ = oracle_lib.topk(q, k, w, k_top=30)
+    q4, w4 = np.repeat(q, 4, axis=0), np.repeat(w, 4, axis=0)
+    i4, s4, _ = oracle_lib.topk_shared(q4, k, w4, k_top=30)
+    assert i4.tolist() == i1[0].tolist()
+    assert s4.tolist() == (4 * s1[0]).tolist()
+
+
+def test_shared_minus_inf_term_excludes_key(oracle_lib):
+    """A key masked (or out of range) for one query only is never selected,
+    whatever the others score; with fewer selectable keys than k_top the row
+    is padded; a ubatch without queries sums to 0 for every key."""
+    q, k, w = li.draw_qkw(3, 40, 2, 8, "f16", True, seed=13)
+    q[:, :, :] = np.abs(q)
+    k[:, :] = np.abs(k)
+    mask = np.zeros((3, 40), np.float16)
+    mask[1, 5] = -np.inf                      # key 5 masked for query 1 only
+    k[5] *= 8                                 # ... though it scores highest
+    ranges = np.array([[0, 40], [0, 40], [0, 30]], np.int32)   # keys 30.. unseen by query 2
+    idx, sc, _ = oracle_lib.topk_shared(q, k, w, mask=mask, kv_range=ranges, k_top=35)
+    chosen = set(idx[idx >= 0].tolist())
+    assert 5 not in chosen and not (chosen & set(range(30, 40)))
+    assert len(chosen) == 29 and idx[29:].tolist() == [-1] * 6 and np.all(sc[29:] == -np.inf)
+    i0, s0, _ = oracle_lib.topk_shared(q[:0], k, w[:0], k_top=4)
+    assert i0.tolist() == [0, 1, 2, 3] and s0.tolist() == [0.0] * 4

@@ -37,6 +37,15 @@ MUTATIONS = {
     "k_scale_wrong_row": ("kd[i] *= (double)k_scale[i / D];", "kd[i] *= (double)k_scale[i % D];"),
     "q_scale_wrong_head": ("qd[i] *= (double)q_scale[t * H + i / D];\n        }\n        for (int h = 0; h < H; ++h)\n            wd[h] = (double)w[t * H + h];\n\n        int64_t n = 0;",
                            "qd[i] *= (double)q_scale[t * H];\n        }\n        for (int h = 0; h < H; ++h)\n            wd[h] = (double)w[t * H + h];\n\n        int64_t n = 0;"),
+    "shared_skips_minus_inf": ("if (isinf(v)) { selectable = 0; break; }                 /* -inf term */",
+                               "if (isinf(v)) { continue; }                 /* -inf term */"),
+    "shared_range_ignored": ("if (s < lo[t] || s >= hi[t]) { selectable = 0; break; }   /* v = -inf */",
+                             "if (0) { selectable = 0; break; }   /* v = -inf */"),
+    "shared_first_query_only": ("for (int64_t t = 0; t < n_tok && selectable; ++t) {",
+                                "for (int64_t t = 0; t < 1 && selectable; ++t) {"),
+    "shared_w_of_first_query": ("double I = head_reduced_score(qd + t * H * D, wd + t * H, kd + s * D, H, D);",
+                                "double I = head_reduced_score(qd + t * H * D, wd, kd + s * D, H, D);"),
+    "shared_max_not_sum": ("U += (double)v;", "U = U > (double)v ? U : (double)v;"),
 }
 
 PINS = [
@@ -51,6 +60,11 @@ PINS = [
     T.test_f8e4m3_decode_exhaustive,
     lambda o: T.test_f8_scaled_equals_dequantised(o, 0),
     T.test_f8_closed_form_single_head_single_dim,
+    *[(lambda s: (lambda o: T.test_shared_bruteforce_exact(o, s)))(s) for s in range(4)],
+    T.test_shared_bruteforce_random,
+    T.test_shared_one_query_is_per_query_topk,
+    T.test_shared_identical_queries_scale,
+    T.test_shared_minus_inf_term_excludes_key,
 ]
 
 
