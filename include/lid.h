@@ -155,6 +155,35 @@ int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, co
                  const int32_t* kv_range, int32_t* idx, float* score, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Shared (per-ubatch) top-k: ONE selection of k_top keys for all the queries
+ * of the call, by the summed score
+ *   U[s] = sum_t v[t,s]       (v as for lid_topk: the masked f32 score; a key
+ *                              outside query t's range, or masked for it, has
+ *                              v = -inf, and then U[s] = -inf: not selectable)
+ *   idx[:] = the k_top keys with the largest U, ordered by U descending and,
+ *            on equal U, by key index ascending; score[:] = their U.
+ * ggml-org llama.cpp PR 22378, the batched-prefill commit: the indexer's
+ * per-query scores are summed over the ubatch (and heads) and one ubatch-wide
+ * top-k is taken, which every query of the ubatch then uses (the pages call it
+ * an approximation whose loss is small for adjacent prefill tokens); the
+ * commit that reverts collapse-Q writes it as top_k(sum_q relu(kv*q)*w).
+ * U is accumulated in f32 over the queries in a fixed order (deterministic);
+ * with no queries (n_tok = 0) U = 0 for every key.
+ *   q, k, w, mask, kv_range  as for lid_topk; H = 64, D = 128, f16 or bf16
+ *                            (other shapes and dtypes: LID_ERR_UNSUPPORTED)
+ *   idx       [k_top]  int32 output (-1 after the selectable keys)
+ *   score     [k_top]  f32 output (-inf after them), or NULL
+ *   workspace device scratch of >= lid_topk_shared_workspace_size(shape)
+ *             bytes, 8-byte aligned (no zero-fill needed): the partial sums
+ *             of U per key and query chunk (O(n_kv), not O(n_tok * n_kv)) and
+ *             the per-chunk sorted lists
+ * k_top, plan and splits: k_top as for lid_topk; plan and splits are ignored.
+ * Asynchronous on `stream`; errors as for lid_topk. */
+size_t lid_topk_shared_workspace_size(const lid_shape* shape);
+int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const float* w,
+                    const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* The plan lid_topk would run for `shape` (a lid_plan value), and through
  * `splits_out` (may be NULL) its key splits per query; negative lid_status if
  * the shape is invalid or unsupported. */

@@ -28,6 +28,7 @@ PLAN_NAMES = {PLAN_GENERIC: "generic", PLAN_PREFILL: "prefill", PLAN_DECODE: "de
 STATUS = {0: "LID_OK", -1: "LID_ERR_INVALID_ARG", -2: "LID_ERR_UNSUPPORTED", -3: "LID_ERR_WORKSPACE",
           -4: "LID_ERR_HIP"}
 EXPORTS = ("lid_topk", "lid_topk_fp8", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores",
+           "lid_topk_shared", "lid_topk_shared_workspace_size",
            "lid_status_string", "lid_last_hip_error", "lid_set_profile_events", "lid_version")
 
 
@@ -72,6 +73,10 @@ def load():
                                      ctypes.c_size_t, vp]
         lib.lid_scores.restype = ctypes.c_int
         lib.lid_scores.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
+        lib.lid_topk_shared.restype = ctypes.c_int
+        lib.lid_topk_shared.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.lid_topk_shared_workspace_size.restype = ctypes.c_size_t
+        lib.lid_topk_shared_workspace_size.argtypes = [ctypes.POINTER(LidShape)]
         lib.lid_topk_plan.restype = ctypes.c_int
         lib.lid_topk_plan.argtypes = [ctypes.POINTER(LidShape), ctypes.POINTER(ctypes.c_int32)]
         lib.lid_status_string.restype = ctypes.c_char_p
@@ -170,6 +175,45 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
     else:
         rc = load().lid_topk(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(mask), _ptr(kv_range), _ptr(idx),
                              _ptr(score), _ptr(workspace), ws_have, stream)
+    if rc != 0:
+        raise LidError(rc)
+    return idx, score
+
+
+def topk_shared(q, k, w, mask=None, kv_range=None, k_top=512, *, idx=None, score=None, want_score=True,
+                workspace=None, stream=None):
+    """Shared (per-ubatch) top-k on the GPU: one row of the k_top keys with the
+    largest U[s] = sum over all queries of the masked score (lid_topk_shared).
+    Returns (idx int32 [k_top], score f32 [k_top] or None)."""
+    import torch
+    if q.dim() != 3 or k.dim() != 2 or w.dim() != 2:
+        raise ValueError("q [n_tok,H,D], k [n_kv,D], w [n_tok,H] expected")
+    n_tok, H, D = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("lid.topk_shared runs on the GPU only (q is on %s)" % dev)
+    for name, t in (("q", q), ("k", k), ("w", w), ("mask", mask), ("kv_range", kv_range)):
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if k.dtype != q.dtype or k.shape[1] != D or w.shape != (n_tok, H) or w.dtype != torch.float32:
+        raise ValueError("dtype/shape mismatch among q, k, w")
+    if mask is not None and (mask.dim() != 2 or mask.shape[0] != n_tok):
+        raise ValueError("mask must be float16 [n_tok, mask_ld]")
+    if kv_range is not None and (kv_range.dtype != torch.int32 or tuple(kv_range.shape) != (n_tok, 2)):
+        raise ValueError("kv_range must be int32 [n_tok, 2]")
+    shape = shape_for(q, k, k_top, mask)
+    if idx is None:
+        idx = torch.empty((k_top,), dtype=torch.int32, device=dev)
+    if score is None and want_score:
+        score = torch.empty((k_top,), dtype=torch.float32, device=dev)
+    ws_bytes = int(load().lid_topk_shared_workspace_size(ctypes.byref(shape)))
+    if ws_bytes and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = load().lid_topk_shared(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(mask), _ptr(kv_range),
+                                _ptr(idx), _ptr(score), _ptr(workspace), ws_have, stream)
     if rc != 0:
         raise LidError(rc)
     return idx, score

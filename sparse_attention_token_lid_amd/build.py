@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblid.so")
-SOURCES = ["lid_api.hip", "k_prefill.hip", "k_decode.hip", "k_merge.hip", "k_generic.hip", "k_scores.hip"]
+SOURCES = ["lid_api.hip", "k_prefill.hip", "k_decode.hip", "k_merge.hip", "k_generic.hip", "k_scores.hip",
+           "k_shared.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

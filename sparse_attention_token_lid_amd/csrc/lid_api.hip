@@ -322,6 +322,105 @@ int lid_scores(const lid_shape* shape, const void* q, const void* k, const float
   return LID_OK;
 }
 
+}  // extern "C"
+
+// ------------------------------------------------------------------ shared top-k
+namespace {
+
+struct SharedPlan {
+  int nqc;        // query chunks (partial sums per key)
+  int qchunk;     // queries per chunk
+  int P;          // selection workgroups (sorted lists) over the keys
+  int ch;         // merge chunk when P > 1
+  size_t ws;      // workspace bytes
+  size_t ws_lists;  // offset of the lists
+};
+
+int make_shared_plan(const lid_shape* s, SharedPlan* sp) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->qk_dtype != LID_F16 && s->qk_dtype != LID_BF16) return LID_ERR_UNSUPPORTED;
+  if (s->n_head != kMfmaHeads || s->head_dim != kMfmaDim) return LID_ERR_UNSUPPORTED;
+  memset(sp, 0, sizeof(*sp));
+  const int64_t groups = cdiv(s->n_kv, kSharedGroupKeys);
+  // enough (key group, query chunk) workgroups for one per CU
+  int64_t nqc = groups > 0 ? cdiv(kCUs, groups) : 1;
+  nqc = nqc < 16 ? nqc : 16;
+  nqc = nqc < (s->n_tok > 0 ? s->n_tok : 1) ? nqc : (s->n_tok > 0 ? s->n_tok : 1);
+  sp->nqc = (int)(nqc < 1 ? 1 : nqc);
+  sp->qchunk = (int)(s->n_tok > 0 ? cdiv(s->n_tok, sp->nqc) : 1);
+  const int64_t P = cdiv(s->n_kv, kSharedListKeys);
+  if (P > kMaxSplits) return LID_ERR_UNSUPPORTED;
+  sp->P = (int)(P < 1 ? 1 : P);
+  if (shared_lists_lds_bytes(s->k_top) > kMaxLds) return LID_ERR_UNSUPPORTED;
+  if (sp->P > 1) {
+    sp->ch = merge_chunk(sp->P, s->k_top);
+    if (merge_lds_bytes(sp->P, s->k_top, sp->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
+  }
+  if (groups * sp->nqc > INT32_MAX) return LID_ERR_UNSUPPORTED;
+  sp->ws_lists = (size_t)cdiv((int64_t)sp->nqc * s->n_kv * 4, 256) * 256;
+  sp->ws = sp->ws_lists + (sp->P > 1 ? (size_t)sp->P * s->k_top * sizeof(uint64_t) : 0);
+  return LID_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lid_topk_shared_workspace_size(const lid_shape* shape) {
+  SharedPlan sp;
+  if (!shape || make_shared_plan(shape, &sp) != LID_OK) return 0;
+  return sp.ws;
+}
+
+int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
+                    const int32_t* kv_range, int32_t* idx, float* score, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!shape) return LID_ERR_INVALID_ARG;
+  SharedPlan sp;
+  int rc = make_shared_plan(shape, &sp);
+  if (rc != LID_OK) return rc;
+  const lid_shape& s = *shape;
+  if (!idx || (s.n_tok > 0 && (!q || !w)) || (s.n_kv > 0 && !k)) return LID_ERR_INVALID_ARG;
+  if (mask && s.mask_ld < s.n_kv) return LID_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(k) & 15)) return LID_ERR_INVALID_ARG;
+  if (sp.ws > 0 && (!workspace || workspace_bytes < sp.ws)) return LID_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 7) return LID_ERR_INVALID_ARG;
+
+  KArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.w = w;
+  a.mask = mask;
+  a.kv_range = kv_range;
+  a.idx = idx;
+  a.score = score;
+  a.scores = reinterpret_cast<float*>(workspace);
+  a.scores_ld = s.n_kv;
+  a.lists = reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(workspace) + sp.ws_lists);
+  a.n_tok = s.n_tok;
+  a.n_kv = s.n_kv;
+  a.mask_ld = mask ? s.mask_ld : 0;
+  a.H = s.n_head;
+  a.D = s.head_dim;
+  a.K = s.k_top;
+  a.P = sp.P;
+  a.dtype = s.qk_dtype;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_shared_scores(a, sp.qchunk, sp.nqc, st)) != hipSuccess) return hip_fail(e);
+  if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_shared_lists(a, sp.nqc, st)) != hipSuccess) return hip_fail(e);
+  if (sp.P > 1) {
+    KArgs m = a;
+    m.n_tok = 1;  // one output row
+    if ((e = launch_merge(m, sp.ch, st)) != hipSuccess) return hip_fail(e);
+  }
+  return LID_OK;
+}
+
 const char* lid_status_string(int status) {
   switch (status) {
     case LID_OK: return "ok";

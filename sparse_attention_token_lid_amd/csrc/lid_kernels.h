@@ -20,7 +20,8 @@ struct KArgs {
   uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1); decode tops
                             // form: [n_tok, P, kDecodeTopsC] split summaries
   uint32_t* raw;            // decode, raw form: [n_tok, raw_ld] ordered scores (0 = no key)
-  float* scores;            // score-only mode: [n_tok, scores_ld] f32 output
+  float* scores;            // score-only mode: [n_tok, scores_ld] f32 output; shared top-k:
+                            // [query chunks, scores_ld] partial sums over the ubatch
   int64_t scores_ld;
   uint32_t* counters;       // finished-workgroup counters (zero between launches): decode [n_tok],
                             // prefill with a fused finish [query blocks]
@@ -41,6 +42,8 @@ constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS 
 constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
 constexpr int kDecodeTopsC = 16;       // decode, tops form: keys in each split's summary
 constexpr int kDecodeTopsMax = 4096;   // decode, tops form: most summary keys per query (P kDecodeTopsC)
+constexpr int kSharedGroupKeys = 256;  // shared top-k: keys per scoring workgroup
+constexpr int kSharedListKeys = 4096;  // shared top-k: keys per selection workgroup (one sorted list each)
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
 constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <= 64 x this keys
 
@@ -54,6 +57,13 @@ size_t prefill_lds_bytes(int nw, int cap);
 // decode finish forms: 0 sorted split lists, 1 raw scores, 2 split summaries
 hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, int form, hipStream_t st);
 size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form);
+
+// shared (per-ubatch) top-k: partial sums of U over nqc query chunks into
+// a.scores [nqc, scores_ld], then a.P sorted lists of a.K keys (or, when a.P
+// == 1, the output row itself)
+hipError_t launch_shared_scores(const KArgs& a, int qchunk, int nqc, hipStream_t st);
+hipError_t launch_shared_lists(const KArgs& a, int nqc, hipStream_t st);
+size_t shared_lists_lds_bytes(int K);
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st);
 size_t merge_lds_bytes(int P, int K, int ch);

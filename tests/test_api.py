@@ -160,3 +160,21 @@ def test_fp8_entry_errors(L):
     assert f(ctypes.byref(sp), 16, 16, 16, 16, 16, None, None, 16, None, None, 0, None) == -2
     assert lib.lid_scores(ctypes.byref(s8), 16, 16, 16, None, None, 16, s8.n_kv, None) == -2
 
+
+
+def test_shared_plan_and_errors(L):
+    """lid_topk_shared: workspace O(query chunks * n_kv + lists), and the
+    argument checks that run before any launch."""
+    lib = L.load()
+    s = shape_of("c3")
+    ws = lib.lid_topk_shared_workspace_size(ctypes.byref(s))
+    assert 16384 * 4 <= ws <= 16 * 16384 * 4 + 4 * 512 * 8 + 256
+    assert ws < s.n_tok * s.n_kv * 4 / 8                     # far below the n_tok x n_kv score matrix
+    f = lib.lid_topk_shared
+    assert f(ctypes.byref(s), 16, 16, 16, None, None, None, None, 16, ws, None) == -1          # no idx
+    assert f(ctypes.byref(s), 16, 16, 16, None, None, 16, None, None, 0, None) == -3           # no workspace
+    assert f(ctypes.byref(s), 8, 16, 16, None, None, 16, None, 16, ws, None) == -1             # q misaligned
+    assert f(ctypes.byref(shape_of("c3", qk_dtype=L.LID_F32)), 16, 16, 16, None, None, 16, None, 16, ws,
+             None) == -2                                                                      # f32: no MFMA path
+    assert f(ctypes.byref(shape_of("c1")), 16, 16, 16, None, None, 16, None, 16, ws, None) == -2  # H=4, D=32
+    assert lib.lid_topk_shared_workspace_size(ctypes.byref(shape_of("c3", k_top=0))) == 0
