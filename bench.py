@@ -51,6 +51,7 @@ PLAN_SOURCES = {
     "decode": ["k_decode.hip", "lid_device.h", "lid_kernels.h", "lid_merge.h", "lid_select.h"],
     "prefill": ["k_prefill.hip", "lid_device.h", "lid_kernels.h"],
     "generic": ["k_generic.hip", "lid_device.h", "lid_kernels.h"],
+    "shared": ["k_shared.hip", "lid_device.h", "lid_kernels.h", "lid_select.h"],
 }
 
 
@@ -158,7 +159,7 @@ def main():
     ap.add_argument("--qk", default="f16", choices=["f16", "fp8"],
                     help="f16: the workload's f16 q and k (the default); fp8: the same values quantised to "
                          "OCP E4M3 with per-row scales (max |row| / 448), run through lid_topk_fp8")
-    ap.add_argument("--mode", default="topk", choices=["topk", "scores"],
+    ap.add_argument("--mode", default="topk", choices=["topk", "scores", "shared"],
                     help="topk: the fused top-k (the default); scores: the score-only mode (lid_scores), "
                          "which writes the n_tok x n_kv f32 scores")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -231,6 +232,16 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
     lib = L.load()
     scores_mode = args.mode == "scores"
+    shared_mode = args.mode == "shared"
+    if shared_mode:
+        # one ubatch-wide selection: every (query, key) pair is scored
+        lib.lid_topk_shared_workspace_size.restype = ctypes.c_size_t
+        ws_bytes = int(lib.lid_topk_shared_workspace_size(ctypes.byref(shape)))
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        idx = torch.empty((wl.k_top,), dtype=torch.int32, device=dev)
+        sc = torch.empty((wl.k_top,), dtype=torch.float32, device=dev)
+        plan, splits = "shared", 1
+        pairs = wl.n_tok * wl.n_kv
     if scores_mode:
         sout = torch.empty((wl.n_tok, wl.n_kv), dtype=torch.float32, device=dev)
         pshape = L.shape_for(q0, k0, wl.k_top, m0, plan=L.PLAN_PREFILL)
@@ -249,7 +260,8 @@ def main():
                           stream))
     log(f"[bench] mode={args.mode} plan={plan} splits={splits} workspace={ws_bytes} B copies={copies} "
         f"({per_copy / 2**20:.1f} MiB each) steps={steps} warmup={warmup}")
-    entry = lib.lid_scores if scores_mode else (lib.lid_topk_fp8 if fp8 else lib.lid_topk)
+    entry = lib.lid_scores if scores_mode else (lib.lid_topk_shared if shared_mode else
+                                                (lib.lid_topk_fp8 if fp8 else lib.lid_topk))
 
     def step(i):
         rc = entry(*calls[i % copies])
@@ -331,7 +343,7 @@ def main():
     if scores_mode:
         assert bool(torch.isfinite(sout[-1]).any()), "no visible score in the last row"
     else:
-        got = idx[0].cpu().numpy()
+        got = (idx if shared_mode else idx[0]).cpu().numpy()
         assert got.max() < wl.n_kv and (got[got >= 0].size == np.unique(got[got >= 0]).size), "invalid top-k row"
     del graph
 
@@ -380,7 +392,7 @@ def main():
         "kernel_hash": kernel_source_hash(plan),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not scores_mode and not fp8:
+    if not args.no_cpu_baseline and not scores_mode and not fp8 and not shared_mode:
         log(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(d, form, args.cpu_seconds)
     print(json.dumps(out), flush=True)
