@@ -8,7 +8,7 @@
 // taken; the later commit that reverts collapse-Q writes it as
 // top_k(sum_q relu(kv * q) * w).
 //
-// Two kernels, then (several key chunks) the split merge of lid_merge.h:
+// Two kernels, then (several key chunks) a merge of the sorted lists:
 //  * shared_scores_kernel: one workgroup per (group of 256 keys, chunk of
 //    queries).  The key group is staged once in LDS (16-byte chunks
 //    XOR-swizzled per row); wavefront w takes queries w, w + 8, ... of the
@@ -22,8 +22,12 @@
 //    as 64-bit keys (ordered U, ~index; 0 = not selectable); the k_top best
 //    are selected and sorted, into the output when one workgroup covers
 //    every key, else into a list for the merge.
+//  * shared_merge_kernel: the round-based list merge of lid_merge.h (each
+//    list here may hold a large share of the answer, so the merge reads
+//    about 4 k_top entries in its first round instead of short prefixes).
 #include "lid_device.h"
 #include "lid_kernels.h"
+#include "lid_merge.h"
 #include "lid_select.h"
 
 namespace lid {
@@ -181,6 +185,11 @@ __global__ __launch_bounds__(BS, 1) void shared_lists_kernel(KArgs a, int nqc) {
   for (int i = threadIdx.x; i < a.K; i += BS) out[i] = sel[i];
 }
 
+__global__ __launch_bounds__(kMergeThreads) void shared_merge_kernel(KArgs a, int ch) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  merge_lists(a, ch, 0, smem);
+}
+
 template <typename F>
 hipError_t set_lds_attr(F* f, bool& done) {
   if (done) return hipSuccess;
@@ -210,6 +219,17 @@ hipError_t launch_shared_scores(const KArgs& a, int qchunk, int nqc, hipStream_t
     if ((e = set_lds_attr(&shared_scores_kernel<1>, done)) != hipSuccess) return e;
     hipLaunchKernelGGL(shared_scores_kernel<1>, grid, dim3(BS), kScoresLds, st, a, qchunk);
   }
+  return hipGetLastError();
+}
+
+size_t shared_merge_lds_bytes(int P, int K, int ch) { return merge_lds_need(P, K, ch); }
+
+hipError_t launch_shared_merge(const KArgs& a, int ch, hipStream_t st) {
+  static bool done = false;
+  hipError_t e = set_lds_attr(&shared_merge_kernel, done);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(shared_merge_kernel, dim3(1), dim3(kMergeThreads), shared_merge_lds_bytes(a.P, a.K, ch), st, a,
+                     ch);
   return hipGetLastError();
 }
 

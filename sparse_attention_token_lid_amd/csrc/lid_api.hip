@@ -355,7 +355,7 @@ int make_shared_plan(const lid_shape* s, SharedPlan* sp) {
   if (shared_lists_lds_bytes(s->k_top) > kMaxLds) return LID_ERR_UNSUPPORTED;
   if (sp->P > 1) {
     sp->ch = merge_chunk(sp->P, s->k_top);
-    if (merge_lds_bytes(sp->P, s->k_top, sp->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
+    if (shared_merge_lds_bytes(sp->P, s->k_top, sp->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
   }
   if (groups * sp->nqc > INT32_MAX) return LID_ERR_UNSUPPORTED;
   sp->ws_lists = (size_t)cdiv((int64_t)sp->nqc * s->n_kv * 4, 256) * 256;
@@ -414,9 +414,7 @@ int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const 
   if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
   if ((e = launch_shared_lists(a, sp.nqc, st)) != hipSuccess) return hip_fail(e);
   if (sp.P > 1) {
-    KArgs m = a;
-    m.n_tok = 1;  // one output row
-    if ((e = launch_merge(m, sp.ch, st)) != hipSuccess) return hip_fail(e);
+    if ((e = launch_shared_merge(a, sp.ch, st)) != hipSuccess) return hip_fail(e);
   }
   return LID_OK;
 }

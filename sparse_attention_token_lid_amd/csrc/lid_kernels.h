@@ -64,6 +64,8 @@ size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form);
 hipError_t launch_shared_scores(const KArgs& a, int qchunk, int nqc, hipStream_t st);
 hipError_t launch_shared_lists(const KArgs& a, int nqc, hipStream_t st);
 size_t shared_lists_lds_bytes(int K);
+hipError_t launch_shared_merge(const KArgs& a, int ch, hipStream_t st);  // a.P lists of a.K -> the output row
+size_t shared_merge_lds_bytes(int P, int K, int ch);
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st);
 size_t merge_lds_bytes(int P, int K, int ch);
