@@ -381,6 +381,7 @@ struct TopsLds {
 };
 __host__ __device__ inline TopsLds tops_lds(int keys_per_wg, int P) {
   static_assert((size_t)kStageBytes >= (4096 + 2048) * 8, "tree buffers fit the stage region");
+  static_assert(2 * kTreeCap + 2 * BS <= 2048, "the block sort's keys and scratch fit the second buffer");
   TopsLds L;
   size_t o = kStageBytes;
   L.arr = o;
@@ -755,13 +756,14 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     finish_lists(a, ch, t, smem);
   } else {
     // The K best of the query from the P summaries (each the sorted kTopsC
-    // best keys of one split).  The merge tree gives the K best candidates,
-    // whose K-th key tau bounds the answer from below.  A split whose
-    // kTopsC-th key is above tau may hold further keys above tau: the
-    // one with the highest such key is scored again into LDS, its K best
-    // replace its summary among the candidates, and the tree runs again,
-    // until no summary is cut short above tau (every key of the answer is
-    // then a candidate).  Each split is re-scored at most once.
+    // best keys of one split).  The K best candidates, sorted (radix cut and
+    // block sort, or the merge tree for at most 1024), have a K-th key tau
+    // that bounds the answer from below.  A split whose kTopsC-th key is
+    // above tau may hold further keys above tau: the one with the highest
+    // such key is scored again into LDS, its K best replace its summary
+    // among the candidates, and the selection runs again, until no summary
+    // is cut short above tau (every key of the answer is then a candidate).
+    // Each split is re-scored at most once.
     const int K = a.K;
     const TopsLds L = tops_lds(keys_per_wg, P);
     uint64_t* cand = reinterpret_cast<uint64_t*>(smem);               // [4096] (stage region)
@@ -786,12 +788,18 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     __syncthreads();
     int mc = m0;
     for (;;) {
-      if (mc > 4 * kTreeCap) {
-        // more than 2048 candidates: a radix select cuts them to the K best
-        // first (fewer vector instructions than sorting them all; measured
-        // slower at 2048 and below), and the tree then only sorts those
-        const int ns = block_select_compact_reg<kDecodeTopsMax / BS>(cand, mc, K, alt, nullptr, shs, red);
-        block_topk_tree_any(alt, cand, ns, K, nullptr, nullptr, best);
+      if (mc > 2 * kTreeCap) {
+        // more than 1024 candidates: a register radix select cuts them to the K
+        // best, which one key per thread then sorts (block bitonic sort, six
+        // LDS stages for 512 keys); measured faster than the merge tree there
+        uint64_t* selk = alt;                 // [kTreeCap]
+        uint64_t* tmps = alt + 2 * kTreeCap;  // [2 BS]
+        const int ns = block_select_compact_reg<kDecodeTopsMax / BS>(cand, mc, K, selk, nullptr, shs, red);
+        for (int i = ns + tid; i < kTreeCap; i += BS) selk[i] = 0ull;
+        __syncthreads();
+        block_sort_desc(selk, kTreeCap, tmps);
+        for (int i = tid; i < kTreeCap; i += BS) best[i] = selk[i];
+        __syncthreads();
       } else {
         block_topk_tree_any(cand, alt, mc, K, nullptr, nullptr, best);
       }
