@@ -453,6 +453,9 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   uint64_t* tmp = sel + next_pow2(a.K);                              // [2 * BS]
   BlockShared* sh = reinterpret_cast<BlockShared*>(tmp + 2 * BS);
   uint32_t* s_last = reinterpret_cast<uint32_t*>(sh + 1);
+  // next 32-key block of the current range for the wavefront that asks first
+  int* s_next = FORM == kFormTops ? reinterpret_cast<int*>(smem + tops_lds(keys_per_wg, a.P).ints + 24)
+                                  : reinterpret_cast<int*>(s_last + 1);
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -505,7 +508,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     // a block needs one 32-bit offset and no clamping, and the loads are
     // unconditional (a load under a branch makes the compiler wait for every
     // load in flight where the paths join).  Offsets stay below 2^22: at most
-    // kDecodeMaxKeys + 32 (NW kDepth) rows.  Without a mask the mask buffer
+    // kDecodeMaxKeys + 32 NW (kDepth + 1) rows.  Without a mask the mask buffer
     // is empty: its loads read nothing and give 0.
     const int64_t row0 = lo + rb0 * KB;
     int64_t nrows = (rb1 - rb0) * KB;
@@ -519,6 +522,20 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
         const_cast<uint16_t*>(a.mask ? a.mask + t * a.mask_ld + row0 : reinterpret_cast<const uint16_t*>(a.w)),
         (short)0, a.mask ? (int)(nrows * 2) : 0, 0x00020000);
     constexpr int kNT = 2;  // non-temporal: the keys are read once
+    // Blocks are handed out dynamically: wavefront w starts with block rb0 +
+    // w, then takes the next one from the workgroup's LDS counter whenever it
+    // loads, so faster wavefronts score more blocks (with a fixed share, the
+    // slowest wavefront of the slowest workgroup set the kernel's end, about
+    // 9 us after the typical one on the 1M-key decode).  Which wavefront
+    // scores a block does not change any result.  Past the range end the
+    // counter hands out blocks >= rb1, whose loads read nothing.
+    if (threadIdx.x == 0) *s_next = NW;
+    __syncthreads();
+    auto grab = [&]() -> int64_t {
+      int v = 0;
+      if (lane == 0) v = __hip_atomic_fetch_add(s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return rb0 + __builtin_amdgcn_readfirstlane(v);
+    };
     auto load_mask = [&](int64_t b) -> uint16_t {
       return __builtin_amdgcn_raw_buffer_load_b16(mrs, (uint32_t)((b - rb0) * KB + m) * 2u, 0, kNT);
     };
@@ -568,29 +585,41 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
       };
 
       // A ring of kDepth register sets: while a block is scored, the loads of
-      // the next kDepth - 1 blocks of this wave are in flight.  Past the end
-      // of the wave's blocks a slot loads from beyond the buffer's range
+      // the next kDepth - 1 blocks of this wave are in flight.  A slot whose
+      // block lies past the range loads from beyond the buffer's range
       // (zeros, no memory access) and is never scored: every load is
       // unconditional.
       const int64_t bs = rb0 + wv;
-      if (hi > lo && bs < rb1) {
-        static_assert(kDepth >= 1, "ring depth");
+      if constexpr (kDepth == 1) {
+        // no ring: load a block, score it, then take the next
+        if (hi > lo) {
+          u32x4 f[8];
+          for (int64_t b = bs; b < rb1; b = grab()) {
+            const uint16_t mb = load_mask(b);
+            load_blk(b, f);
+            score_blk(b, f, mb);
+          }
+        }
+      } else if (hi > lo && bs < rb1) {
+        static_assert(kDepth >= 2, "ring depth");
         u32x4 f[kDepth][8];
         uint16_t mk[kDepth];
+        int64_t bid[kDepth];
 #pragma unroll
         for (int d = 0; d < kDepth - 1; ++d) {
-          mk[d] = load_mask(bs + d * NW);
-          load_blk(bs + d * NW, f[d]);
+          bid[d] = d == 0 ? bs : grab();
+          mk[d] = load_mask(bid[d]);
+          load_blk(bid[d], f[d]);
         }
-        for (int64_t b = bs; b < rb1; b += kDepth * NW) {
+        for (bool more = true; more;) {
 #pragma unroll
           for (int d = 0; d < kDepth; ++d) {
-            const int64_t bc = b + d * NW;  // scored now, from slot d
-            if (bc >= rb1) break;
-            const int64_t bl = bc + (kDepth - 1) * NW;  // loaded now, into the slot freed last
-            mk[(d + kDepth - 1) % kDepth] = load_mask(bl);
-            load_blk(bl, f[(d + kDepth - 1) % kDepth]);
-            score_blk(bc, f[d], mk[d]);
+            if (bid[d] >= rb1) { more = false; break; }  // slot d holds the block scored now
+            const int dl = (d + kDepth - 1) % kDepth;  // the slot freed last: load the next block
+            bid[dl] = grab();
+            mk[dl] = load_mask(bid[dl]);
+            load_blk(bid[dl], f[dl]);
+            score_blk(bid[d], f[d], mk[d]);
           }
         }
       }
@@ -659,20 +688,22 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
       if (hi > lo && bs < rb1) {
         u32x4 f[kDepth8][4];
         uint16_t mk[kDepth8];
+        int64_t bid[kDepth8];
 #pragma unroll
         for (int d = 0; d < kDepth8 - 1; ++d) {
-          mk[d] = load_mask(bs + d * NW);
-          load_blk8(bs + d * NW, f[d]);
+          bid[d] = d == 0 ? bs : grab();
+          mk[d] = load_mask(bid[d]);
+          load_blk8(bid[d], f[d]);
         }
-        for (int64_t b = bs; b < rb1; b += kDepth8 * NW) {
+        for (bool more = true; more;) {
 #pragma unroll
           for (int d = 0; d < kDepth8; ++d) {
-            const int64_t bc = b + d * NW;
-            if (bc >= rb1) break;
-            const int64_t bl = bc + (kDepth8 - 1) * NW;
-            mk[(d + kDepth8 - 1) % kDepth8] = load_mask(bl);
-            load_blk8(bl, f[(d + kDepth8 - 1) % kDepth8]);
-            score_blk8(bc, f[d], mk[d]);
+            if (bid[d] >= rb1) { more = false; break; }
+            const int dl = (d + kDepth8 - 1) % kDepth8;
+            bid[dl] = grab();
+            mk[dl] = load_mask(bid[dl]);
+            load_blk8(bid[dl], f[dl]);
+            score_blk8(bid[d], f[d], mk[d]);
           }
         }
       }
