@@ -365,12 +365,12 @@ __device__ __forceinline__ void select_raw(const KArgs& a, int64_t t, int n, int
 // Forms of the per-query finish (chosen by the host, see lid_api.hip).
 constexpr int kFormLists = 0;  // every split writes its sorted k_top best; the last merges them
 constexpr int kFormRaw = 1;    // every split writes raw ordered scores; the last selects from all
-constexpr int kFormTops = 2;   // every split writes its sorted kDecodeTopsC best; the last merges
-                               // them and re-scores a split only when its summary is too short
-constexpr int kTopsC = kDecodeTopsC;
-static_assert(NW * kTopsC == 2 * kWave, "the split summary combines two keys per lane");
-constexpr int kTopsBuf = kWave - kTopsC;             // candidate slots per wavefront
-constexpr int kTopsArrMin = NW * kTopsC + NW * kTopsBuf;  // summaries + buffers
+constexpr int kFormTops = 2;   // every split writes its sorted 16 best; the last merges them and
+                               // re-scores a split only when its summary is too short
+constexpr int kFormTops8 = 3;  // the same with summaries of 8 keys (twice as many splits)
+template <int FORM> constexpr int tops_c() { return FORM == kFormTops8 ? 8 : 16; }  // keys per summary
+static_assert(NW * 16 == 2 * kWave && NW * 8 == kWave, "a split summary combines two or one keys per lane");
+constexpr int kTopsArrMin = NW * kWave;  // summaries + wavefront buffers (C + (64 - C) per wavefront)
 
 // LDS of the tops form.  The stage region (scoring) also holds the merge
 // tree's candidates and its second buffer; `arr` holds the wave summaries and
@@ -379,7 +379,7 @@ constexpr int kTopsArrMin = NW * kTopsC + NW * kTopsBuf;  // summaries + buffers
 struct TopsLds {
   size_t arr, best, sh, red, lastc, flags, ints, total;
 };
-__host__ __device__ inline TopsLds tops_lds(int keys_per_wg, int P) {
+__host__ __device__ inline TopsLds tops_lds(int keys_per_wg, int P) {  // (either summary size)
   static_assert((size_t)kStageBytes >= (4096 + 2048) * 8, "tree buffers fit the stage region");
   static_assert(2 * kTreeCap + 2 * BS <= 2048, "the block sort's keys and scratch fit the second buffer");
   TopsLds L;
@@ -417,6 +417,7 @@ struct TopsState {
   int nbuf;        // wave-uniform
   uint64_t* buf;   // [kTopsBuf] this wavefront's LDS buffer
 };
+template <int kTopsC>
 __device__ __forceinline__ void tops_flush(TopsState& st, int lane) {
   __builtin_amdgcn_wave_barrier();
   uint64_t x[1] = {lane < kTopsC ? st.top : (lane - kTopsC < st.nbuf ? st.buf[lane - kTopsC] : 0ull)};
@@ -428,13 +429,15 @@ __device__ __forceinline__ void tops_flush(TopsState& st, int lane) {
   st.th = ((uint64_t)thi << 32) | tlo;
   __builtin_amdgcn_wave_barrier();
 }
+template <int kTopsC>
 __device__ __forceinline__ void tops_insert(TopsState& st, uint64_t key, int lane) {
+  constexpr int kTopsBuf = kWave - kTopsC;  // candidate slots per wavefront
   bool c = lane >= 32 && key > st.th;
   uint64_t mk = ballot(c);
   if (mk == 0ull) return;
   int n = __popcll(mk);
   if (st.nbuf + n > kTopsBuf) {
-    tops_flush(st, lane);
+    tops_flush<kTopsC>(st, lane);
     c = lane >= 32 && key > st.th;
     mk = ballot(c);
     if (mk == 0ull) return;
@@ -446,6 +449,9 @@ __device__ __forceinline__ void tops_insert(TopsState& st, uint64_t key, int lan
 
 template <int DT, int FORM>
 __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg, int ch) {
+  constexpr bool TOPS = FORM == kFormTops || FORM == kFormTops8;
+  constexpr int kTopsC = tops_c<FORM>();
+  constexpr int kTopsBuf = kWave - kTopsC;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* stage_all = reinterpret_cast<uint16_t*>(smem);           // [NW][KB * D]
   uint64_t* arr = reinterpret_cast<uint64_t*>(smem + kStageBytes);   // [keys_per_wg] (lists form)
@@ -454,7 +460,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   BlockShared* sh = reinterpret_cast<BlockShared*>(tmp + 2 * BS);
   uint32_t* s_last = reinterpret_cast<uint32_t*>(sh + 1);
   // next 32-key block of the current range for the wavefront that asks first
-  int* s_next = FORM == kFormTops ? reinterpret_cast<int*>(smem + tops_lds(keys_per_wg, a.P).ints + 24)
+  int* s_next = TOPS ? reinterpret_cast<int*>(smem + tops_lds(keys_per_wg, a.P).ints + 24)
                                   : reinterpret_cast<int*>(s_last + 1);
 
   const int tid = threadIdx.x;
@@ -731,17 +737,23 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     uint64_t* tw = reinterpret_cast<uint64_t*>(smem + L.arr);  // [NW][kTopsC], then [NW][kTopsBuf]
     TopsState st{0ull, 0ull, 0, tw + NW * kTopsC + wv * kTopsBuf};
     score_range(std::integral_constant<int, kRingDepth>{}, b0, b1,
-                [&](int64_t b, int64_t s, float v) { tops_insert(st, valid_key(s, v), lane); });
-    if (st.nbuf) tops_flush(st, lane);
+                [&](int64_t b, int64_t s, float v) { tops_insert<kTopsC>(st, valid_key(s, v), lane); });
+    if (st.nbuf) tops_flush<kTopsC>(st, lane);
     if (lane < kTopsC) tw[wv * kTopsC + lane] = st.top;
     __syncthreads();
     if (wv == 0) {
-      uint64_t x[2] = {tw[2 * lane], tw[2 * lane + 1]};
-      wave_sort_reg<2>(x, lane);
       uint64_t* out = a.lists + ((size_t)t * P + p) * kTopsC;
-      if (lane < kTopsC / 2) {
-        __hip_atomic_store(&out[2 * lane], x[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&out[2 * lane + 1], x[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if constexpr (NW * kTopsC == 2 * kWave) {
+        uint64_t x[2] = {tw[2 * lane], tw[2 * lane + 1]};
+        wave_sort_reg<2>(x, lane);
+        if (lane < kTopsC / 2) {
+          __hip_atomic_store(&out[2 * lane], x[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&out[2 * lane + 1], x[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else {
+        uint64_t x[1] = {tw[lane]};
+        wave_sort_reg<1>(x, lane);
+        if (lane < kTopsC) __hip_atomic_store(&out[lane], x[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -773,7 +785,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
   // back or invalidating them, which device-scope fences would do); every
   // store has completed (vmcnt(0)) before the counter moves.
   uint32_t* s_flag = s_last;
-  if constexpr (FORM == kFormTops) s_flag = reinterpret_cast<uint32_t*>(smem + tops_lds(keys_per_wg, P).ints);
+  if constexpr (TOPS) s_flag = reinterpret_cast<uint32_t*>(smem + tops_lds(keys_per_wg, P).ints);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0)
@@ -890,13 +902,14 @@ template <int DT>
 hipError_t launch_dt(const KArgs& a, int keys_per_wg, int ch, int form, hipStream_t st) {
   if (form == kFormRaw) return launch_one<DT, kFormRaw>(a, keys_per_wg, ch, st);
   if (form == kFormTops) return launch_one<DT, kFormTops>(a, keys_per_wg, ch, st);
+  if (form == kFormTops8) return launch_one<DT, kFormTops8>(a, keys_per_wg, ch, st);
   return launch_one<DT, kFormLists>(a, keys_per_wg, ch, st);
 }
 
 }  // namespace
 
 size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form) {
-  if (form == kFormTops) return tops_lds(keys_per_wg, P).total;
+  if (form == kFormTops || form == kFormTops8) return tops_lds(keys_per_wg, P).total;
   const bool raw = form == kFormRaw;
   const size_t scoring = (size_t)kStageBytes + (size_t)keys_per_wg * 8 + (size_t)next_pow2(K) * 8 + 2 * BS * 8 +
                          sizeof(BlockShared) + 16;

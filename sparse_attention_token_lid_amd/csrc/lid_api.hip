@@ -15,7 +15,7 @@ using namespace lid;
 constexpr int kMaxTopK = 1024;
 constexpr int kMaxSplits = 1024;
 constexpr int kDecodeMaxTok = 4;       // auto plan: at most this many queries use the decode kernel
-constexpr int kDecodeKeysPerSplit = 256;
+constexpr int kDecodeKeysPerSplit = 128;
 constexpr int64_t kCUs = 256;          // MI355X compute units
 constexpr int kDecodeMaxSplits = 256;  // bounds the decode workspace independently of n_kv
 constexpr size_t kMaxLds = 160 * 1024;
@@ -29,8 +29,8 @@ struct Plan {
   int keys_per_wg;  // decode: LDS key slots per workgroup
   int ch;           // merge: entries per list per round
   int form;         // decode finish: 0 sorted split lists, 1 raw scores (the last workgroup
-                    // selects from all of them), 2 split summaries (the best kDecodeTopsC keys
-                    // of every split; a split is scored again if its summary is too short)
+                    // selects from all of them), 2 / 3 split summaries (the best 16 / 8 keys of
+                    // every split; a split is scored again if its summary is too short)
   int fuse;         // prefill, P > 1: the scoring kernel finishes from the split lists itself
                     // (1: merging sorted lists, 2: selecting from unsorted ones)
   int64_t raw_ld;   // decode, raw form: scores per query row
@@ -137,12 +137,16 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (kp > kDecodeMaxKeys) return LID_ERR_UNSUPPORTED;
     pl->keys_per_wg = (int)kp;
     const int64_t span = cdiv(s->n_kv, 32) * 32;  // longest visible range, in 32-key blocks
-    // summaries when the merge tree applies and P kDecodeTopsC holds about 4 K
-    // keys (then a split rarely holds more than kDecodeTopsC of the answer);
-    // else raw scores for short ranges, sorted split lists for long ones
-    const bool tops = P >= 2 && next_pow2(K) == kTreeCapHost && (int64_t)P * kDecodeTopsC <= kDecodeTopsMax &&
-                      (int64_t)P * kDecodeTopsC >= 4LL * K;
-    pl->form = tops ? 2 : (span <= kRawMax ? 1 : 0);
+    // summaries of C keys per split when the finish's selection applies and
+    // 4 K <= P C <= 4096 (then a split rarely holds more than C of the
+    // answer): C = 8 when the splits are that many, else 16; otherwise raw
+    // scores for short ranges, sorted split lists for long ones
+    int tc = 0;
+    if (P >= 2 && next_pow2(K) == kTreeCapHost) {
+      for (int c : {8, kDecodeTopsC})
+        if (!tc && (int64_t)P * c >= 4LL * K && (int64_t)P * c <= kDecodeTopsMax) tc = c;
+    }
+    pl->form = tc == 8 ? 3 : (tc ? 2 : (span <= kRawMax ? 1 : 0));
     if (P > 1 && pl->form == 0) pl->ch = merge_chunk(P, K);
     if (decode_lds_bytes(pl->keys_per_wg, K, P, pl->ch, pl->form) > kMaxLds) return LID_ERR_UNSUPPORTED;
     // workspace: per-query counters (zero between launches), then the raw
@@ -151,8 +155,8 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (pl->form == 1) {
       pl->raw_ld = cdiv(span, 64) * 64;
       pl->ws = pl->ws_data + (size_t)s->n_tok * pl->raw_ld * sizeof(uint32_t);
-    } else if (pl->form == 2) {
-      pl->ws = pl->ws_data + (size_t)s->n_tok * P * kDecodeTopsC * sizeof(uint64_t);
+    } else if (pl->form >= 2) {
+      pl->ws = pl->ws_data + (size_t)s->n_tok * P * tc * sizeof(uint64_t);
     } else {
       pl->ws = pl->ws_data + (P > 1 ? (size_t)s->n_tok * P * K * sizeof(uint64_t) : 0);
     }

@@ -17,8 +17,8 @@ struct KArgs {
   const int32_t* kv_range;  // [n_tok, 2], or null
   int32_t* idx;             // [n_tok, K]
   float* score;             // [n_tok, K], or null
-  uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1); decode tops
-                            // form: [n_tok, P, kDecodeTopsC] split summaries
+  uint64_t* lists;          // [n_tok, P, K] per-split sorted candidate keys (P > 1); decode summary
+                            // forms: [n_tok, P, C] split summaries (C = 16 or 8)
   uint32_t* raw;            // decode, raw form: [n_tok, raw_ld] ordered scores (0 = no key)
   float* scores;            // score-only mode: [n_tok, scores_ld] f32 output; shared top-k:
                             // [query chunks, scores_ld] partial sums over the ubatch
@@ -40,8 +40,8 @@ constexpr int kMfmaDim = 128;
 constexpr int kPrefillTile = 128;      // keys per LDS tile
 constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS bound)
 constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
-constexpr int kDecodeTopsC = 16;       // decode, tops form: keys in each split's summary
-constexpr int kDecodeTopsMax = 4096;   // decode, tops form: most summary keys per query (P kDecodeTopsC)
+constexpr int kDecodeTopsC = 16;       // decode, summary forms: keys in each split's summary (16, or 8)
+constexpr int kDecodeTopsMax = 4096;   // decode, summary forms: most summary keys per query (P C)
 constexpr int kSharedGroupKeys = 256;  // shared top-k: keys per scoring workgroup
 constexpr int kSharedListKeys = 4096;  // shared top-k: keys per selection workgroup (one sorted list each)
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
@@ -54,7 +54,7 @@ hipError_t launch_scores_fill(const KArgs& a, hipStream_t st);     // -inf outsi
 hipError_t launch_generic_scores(const KArgs& a, hipStream_t st);  // score-only mode, any shape
 size_t prefill_lds_bytes(int nw, int cap);
 
-// decode finish forms: 0 sorted split lists, 1 raw scores, 2 split summaries
+// decode finish forms: 0 sorted split lists, 1 raw scores, 2 / 3 split summaries of 16 / 8 keys
 hipError_t launch_decode(const KArgs& a, int keys_per_wg, int ch, int form, hipStream_t st);
 size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form);
 

@@ -62,16 +62,19 @@ def test_auto_plans_and_workspace(L, name, plan):
     lists = wl.n_tok * splits * wl.k_top * 8 if splits > 1 else 0
     if plan == "decode":
         # per-query counters (256-byte rounded), then the split summaries
-        # (16 keys per split, when 16 splits hold 4 k_top to 4096 keys and
-        # 256 < k_top <= 512), else every 32-bit score of the query (ranges up
-        # to 32768 keys), else the split lists
+        # (8 or 16 keys per split, the first size with which the splits hold
+        # 4 k_top to 4096 keys, 256 < k_top <= 512), else every 32-bit score of
+        # the query (ranges up to 32768 keys), else the split lists
         counters = -(-wl.n_tok * 4 // 256) * 256
         span = -(-wl.n_kv // 32) * 32
         raw = wl.n_tok * (-(-span // 64) * 64) * 4
-        tops = 256 < wl.k_top <= 512 and 4 * wl.k_top <= 16 * splits <= 4096
-        summaries = wl.n_tok * splits * 16 * 8
-        assert ws == counters + (summaries if tops else raw if span <= 32768 else lists)
-        assert tops  # both decode workloads (k_top 512, 128 and 256 splits)
+        tc = 0
+        for c in (8, 16):
+            if not tc and 256 < wl.k_top <= 512 and 4 * wl.k_top <= c * splits <= 4096:
+                tc = c
+        summaries = wl.n_tok * splits * tc * 8
+        assert ws == counters + (summaries if tc else raw if span <= 32768 else lists)
+        assert tc == 8  # both decode workloads (k_top 512, 256 splits of 8-key summaries)
     elif splits > 1:
         # per-query-block counters (8 queries per block at k_top <= 512),
         # then the split lists

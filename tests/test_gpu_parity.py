@@ -105,16 +105,16 @@ def test_prefill_split_finish_forms(lid, splits, k_top):
     parity(lid, q, k, w, None, ranges, k_top, "f16", 2, splits, exact=True, label=f"prefill-splits/k{k_top}")
 
 
-@pytest.mark.parametrize("splits", [64, 0])
+@pytest.mark.parametrize("splits", [64, 128, 0])
 @pytest.mark.parametrize("n_above,n_tied", [(400, 3000), (100, 1500), (0, 600), (300, 5000)])
 def test_decode_raw_many_candidates(lid, n_above, n_tied, splits):
     """Decode over 32768 keys when the k_top-th score is shared by many keys:
     n_above distinct larger scores, then n_tied keys with one equal score,
     the rest 0.  The tied keys must be taken in index order.  With 64 splits
     this is the raw-score finish, driven through candidate sets of up to
-    4096 keys (and, past that, through the tie cut); with the library's 128
-    splits, the split summaries, where the tied splits are scored again.
-    Bit exact."""
+    4096 keys (and, past that, through the tie cut); with 128 splits, the
+    16-key split summaries, and with the library's 256 splits the 8-key
+    ones, where the tied splits are scored again.  Bit exact."""
     n_kv = 32768
     rng = np.random.default_rng(n_above + n_tied)
     q = np.zeros((1, 64, 128), np.float32)
@@ -131,15 +131,16 @@ def test_decode_raw_many_candidates(lid, n_above, n_tied, splits):
            label=f"decode-raw/ties{n_tied}")
 
 
-@pytest.mark.parametrize("splits", [128, 0])
+@pytest.mark.parametrize("splits", [64, 127, 128, 0])
 @pytest.mark.parametrize("start,n_cluster", [(1000, 700), (7000, 5120), (0, 0)])
 def test_decode_lists_clustered(lid, start, n_cluster, splits):
     """Decode over 65536 keys when the best keys crowd into a few splits.
-    With 128 splits (sorted split lists of 512 keys each): their lists are
-    read further and further (700 keys over 2 splits), or the candidates
-    outgrow the tree and the round-based merge takes over (5120 keys over 10
-    splits).  With the library's 256 splits (summaries of 16 keys): the
-    crowded splits are scored again, one after another.  Bit exact."""
+    With 64 or 127 splits (sorted split lists of 512 keys each): their lists
+    are read further and further (700 keys over 1-2 splits), or the
+    candidates outgrow the tree and the round-based merge takes over (5120
+    keys over 5-10 splits).  With 128 splits (summaries of 16 keys) and the
+    library's 256 (summaries of 8): the crowded splits are scored again, one
+    after another.  Bit exact."""
     n_kv = 65536
     rng = np.random.default_rng(start + n_cluster)
     q = np.zeros((1, 64, 128), np.float32)
@@ -152,13 +153,13 @@ def test_decode_lists_clustered(lid, start, n_cluster, splits):
            label=f"decode-lists/cluster{n_cluster}")
 
 
-@pytest.mark.parametrize("n_kv,skew,splits", [(300000, False, 100), (1048576, True, 200), (300000, False, 0),
-                                               (1048576, True, 0)])
+@pytest.mark.parametrize("n_kv,skew,splits", [(300000, False, 100), (300000, True, 120), (1048576, True, 200),
+                                               (300000, False, 0), (1048576, True, 0)])
 def test_decode_lists_superset(lid, n_kv, skew, splits):
-    """Decode over long ranges.  With 100 or 200 splits, sorted split lists:
+    """Decode over long ranges.  With 100 or 120 splits, sorted split lists:
     ragged splits of ~3000 keys; and splits whose first 512 keys score 100x
-    lower, so every split cuts its list by a block select.  With the
-    library's 256 splits, summaries of 16 keys per split."""
+    lower, so every split cuts its list by a block select.  With 200 splits,
+    summaries of 16 keys per split; with the library's 256, of 8."""
     q, k, w = li.draw_qkw(1, n_kv, 64, 128, "f16", True, seed=n_kv % 97)
     if skew:
         k = k.astype(np.float32)
@@ -193,11 +194,13 @@ def _one_head_inputs(n_tok, n_kv, seed):
     return q, k, w, rng
 
 
+@pytest.mark.parametrize("splits", [0, 128])
 @pytest.mark.parametrize("case", ["ties", "few-valid", "spread", "dtypes"])
-def test_decode_tops_rescore(lid, case):
-    """Decode with split summaries (the best 16 keys of every split; the
-    library's 256 splits over 65536 keys): inputs whose answer is not covered
-    by the summaries, so the finish must score splits again.  Bit exact.
+def test_decode_tops_rescore(lid, case, splits):
+    """Decode with split summaries (the best 8 keys of each of the library's
+    256 splits over 65536 keys, or the best 16 of 128 splits): inputs whose
+    answer is not covered by the summaries, so the finish must score splits
+    again.  Bit exact.
      - ties: q = 0, every score is +0 and the answer is the first 512 keys
        (splits 0 and 1 in full);
      - few-valid: one query sees keys [100, 3000) through its range, one
@@ -209,7 +212,7 @@ def test_decode_tops_rescore(lid, case):
     if case == "ties":
         q, k, w = exact_inputs(2, n_kv, seed=5)
         q[0] = 0
-        parity(lid, q, k, w, None, None, 512, "f16", 3, 0, exact=True, label="decode-tops/ties")
+        parity(lid, q, k, w, None, None, 512, "f16", 3, splits, exact=True, label="decode-tops/ties")
         return
     if case == "few-valid":
         q, k, w, rng = _one_head_inputs(3, n_kv, seed=6)
@@ -218,13 +221,13 @@ def test_decode_tops_rescore(lid, case):
         mask[1, :] = 0xFC00
         mask[1, 60000:63000] = 0
         ranges = np.array([[100, 3000], [0, n_kv], [0, n_kv]], np.int32)
-        parity(lid, q.astype(np.float16), k.astype(np.float16), w, mask, ranges, 512, "f16", 3, 0, exact=True,
+        parity(lid, q.astype(np.float16), k.astype(np.float16), w, mask, ranges, 512, "f16", 3, splits, exact=True,
                label="decode-tops/few-valid")
         return
     q, k, w, rng = _one_head_inputs(1, n_kv, seed=7)
     k[:, 0] = rng.integers(-8, 100, n_kv)           # scores 0..99 elsewhere
-    splits = rng.choice(256, 13, replace=False)
-    for j, sp in enumerate(splits):
+    chosen = rng.choice(256, 13, replace=False)   # 256-key ranges
+    for j, sp in enumerate(chosen):
         pos = sp * 256 + rng.choice(256, 40, replace=False)
         k[pos, 0] = 200 + 40 * j + np.arange(40)    # distinct, above everything else
     dtype = "bf16" if case == "dtypes" else "f16"
@@ -232,7 +235,7 @@ def test_decode_tops_rescore(lid, case):
         qq, kk = li._round_qk(q, "bf16"), li._round_qk(k, "bf16")
     else:
         qq, kk = q.astype(np.float16), k.astype(np.float16)
-    parity(lid, qq, kk, w, None, None, 512, dtype, 3, 0, exact=True, label=f"decode-tops/spread-{dtype}")
+    parity(lid, qq, kk, w, None, None, 512, dtype, 3, splits, exact=True, label=f"decode-tops/spread-{dtype}")
 
 
 @pytest.mark.parametrize("plan,splits", [(2, 0), (2, 1), (2, 4), (3, 0), (3, 3), (1, 0)])
