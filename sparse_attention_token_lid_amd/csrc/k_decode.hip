@@ -837,7 +837,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
         // LDS stages for 512 keys); measured faster than the merge tree there
         uint64_t* selk = alt;                 // [kTreeCap]
         uint64_t* tmps = alt + 2 * kTreeCap;  // [2 BS]
-        const int ns = block_select_compact_reg<kDecodeTopsMax / BS>(cand, mc, K, selk, nullptr, shs, red);
+        const int ns = block_select_compact_any(cand, mc, K, selk, nullptr, shs, red);  // registers sized to mc
         for (int i = ns + tid; i < kTreeCap; i += BS) selk[i] = 0ull;
         __syncthreads();
         block_sort_desc(selk, kTreeCap, tmps);
