@@ -13,7 +13,8 @@
 //    queries).  The key group is staged once in LDS (16-byte chunks
 //    XOR-swizzled per row); wavefront w takes queries w, w + 8, ... of the
 //    chunk, scores the 256 keys with 32x32x16 MFMAs (q fragments in
-//    registers, the same layout as the decode kernel), applies ReLU, the
+//    registers, the same layout as the decode kernel, the next query's
+//    loaded while the current one is scored), applies ReLU, the
 //    head weights, the head sum and the mask, and adds v into one f32 sum
 //    per key (in its own LDS row).  The eight wavefronts' sums are added in
 //    wavefront order and written as the chunk's partial sums [QC, n_kv].
@@ -59,7 +60,7 @@ constexpr int BS = NW * kWave;
 constexpr int KG = kSharedGroupKeys;  // keys per scoring workgroup
 constexpr int NB = KG / 32;           // 32-key MFMA column blocks
 constexpr int kListKeys = kSharedListKeys;
-constexpr size_t kScoresLds = (size_t)KG * D * 2 + (size_t)NW * KG * 4;
+constexpr size_t kScoresLds = (size_t)KG * D * 2 + (size_t)NW * KG * 4 + (size_t)NW * KG * 2;
 static_assert(BS == kSelThreads, "the list kernel runs the block selection");
 static_assert(KG <= BS && (KG * D / 8) % BS == 0, "staging and the final sum");
 
@@ -70,6 +71,7 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* kt = reinterpret_cast<uint16_t*>(smem);                          // [KG][D]
   float* part = reinterpret_cast<float*>(smem + (size_t)KG * D * 2);         // [NW][KG]
+  uint16_t* mlds = reinterpret_cast<uint16_t*>(part + NW * KG);              // [NW][KG] mask entries
   const int tid = threadIdx.x, wv = tid / kWave, lane = tid & (kWave - 1);
   const int g = lane >> 5, m = lane & 31;
   const int64_t ngroups = (a.n_kv + KG - 1) / KG;
@@ -96,19 +98,41 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
 
   using M = MfmaS<DT>;
   using T = typename M::T;
-  for (int64_t t = t0 + wv; t < t1; t += NW) {
-    T A[2][8];
-    float wr[2][16];
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + t * H * D;
+  // q fragments (16 KiB) and the 256 mask entries of a query: loaded one
+  // query ahead into the other register set, so the loads of the next query
+  // fly while the current one is scored.  The mask row is read through a
+  // buffer resource of the key group's entries: past n_kv, or without a
+  // mask (an empty buffer), the loads return 0 and read nothing, so they are
+  // unconditional.
+  T A[2][8], An[2][8];
+  uint32_t M4[4], M4n[4];
+  uint16_t* mrow = mlds + wv * KG;
+  auto load_q = [&](int64_t t, T (&Aq)[2][8], uint32_t (&mq)[4]) {
+    const int64_t tc = t < t1 ? t : t0;  // past the chunk: any valid row (not used)
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + tc * H * D;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        A[rb][j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j));
+        Aq[rb][j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(qrow + (32 * rb + m) * D + 64 * g + 8 * j));
+    const int64_t nm = a.n_kv - s0 < KG ? a.n_kv - s0 : KG;
+    const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.mask ? a.mask + tc * a.mask_ld + s0 : reinterpret_cast<const uint16_t*>(a.w)),
+        (short)0, a.mask ? (int)(nm * 2) : 0, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mq[i] = __builtin_amdgcn_raw_buffer_load_b16(mr, (uint32_t)(lane + kWave * i) * 2u, 0, 0);
+  };
+  // score query t (its fragments in Aq, mask entries in mq) against the key group
+  auto process = [&](int64_t t, const T (&Aq)[2][8], const uint32_t (&mq)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mrow[lane + kWave * i] = (uint16_t)mq[i];
+    __builtin_amdgcn_wave_barrier();
+    float wq[2][16];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) wr[rb][jj] = a.w[t * H + 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3)];
+      for (int jj = 0; jj < 16; ++jj) wq[rb][jj] = a.w[t * H + 32 * rb + 8 * (jj >> 2) + 4 * g + (jj & 3)];
     int64_t lo = 0, hi = a.n_kv;
     if (a.kv_range) {
       const int64_t l0 = a.kv_range[2 * t], h0 = a.kv_range[2 * t + 1];
@@ -123,24 +147,34 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const T bf = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + swz(32 * b + m, 8 * g + j)));
-        acc0 = M::run(A[0][j], bf, acc0);
-        acc1 = M::run(A[1][j], bf, acc1);
+        acc0 = M::run(Aq[0][j], bf, acc0);
+        acc1 = M::run(Aq[1][j], bf, acc1);
       }
       // sum_h w_h relu(S[h, key]) over this lane's 32 heads, then the other 32
       float p = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p = __builtin_fmaf(wr[0][e], relu(acc0[e]), p);
-        p = __builtin_fmaf(wr[1][e], relu(acc1[e]), p);
+        p = __builtin_fmaf(wq[0][e], relu(acc0[e]), p);
+        p = __builtin_fmaf(wq[1][e], relu(acc1[e]), p);
       }
       const float tot = p + __uint_as_float(xor_lane_u32<32>(__float_as_uint(p)));
       const int64_t s = s0 + 32 * b + m;
-      const int64_t sc = s < a.n_kv ? s : a.n_kv - 1;
-      const uint16_t mb = a.mask ? a.mask[t * a.mask_ld + sc] : (uint16_t)0;
+      const uint16_t mb = mrow[32 * b + m];
       const float v = (tot + f16_bits_to_f32(mb)) + 0.0f;
       const bool ok = s >= lo && s < hi && v != -__builtin_inff();
       if (g == 0) prow[32 * b + m] += ok ? v : -__builtin_inff();
     }
+    __builtin_amdgcn_wave_barrier();  // every lane has read mrow before the next query's entries
+  };
+  // two register sets, alternating: the next query's loads fly while the
+  // current one is scored
+  if (t0 + wv < t1) load_q(t0 + wv, A, M4);
+  for (int64_t t = t0 + wv; t < t1; t += 2 * NW) {
+    load_q(t + NW, An, M4n);
+    process(t, A, M4);
+    if (t + NW >= t1) break;
+    load_q(t + 2 * NW, A, M4);
+    process(t + NW, An, M4n);
   }
   __syncthreads();
   if (tid < KG) {
