@@ -60,6 +60,8 @@ def load_library(path: str):
                                            vp, vp, vp, i32]
     lib.lid_oracle_topk_shared.restype = ctypes.c_int
     lib.lid_oracle_topk_shared.argtypes = [i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, i64, vp, vp, vp, vp, i32]
+    lib.lid_oracle_sparse_attn.restype = ctypes.c_int
+    lib.lid_oracle_sparse_attn.argtypes = [i64, i64, i32, i32, i32, i32, vp, vp, vp, ctypes.c_double, vp, i32]
     lib.lid_oracle_scores_scaled.restype = ctypes.c_int
     lib.lid_oracle_scores_scaled.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp, i32]
     lib.lid_oracle_f8e4m3_to_f64.restype = ctypes.c_double
@@ -95,6 +97,9 @@ class Oracle:
 
     def topk_shared(self, *a, **kw):
         return topk_shared(*a, _lib=self._lib, **kw)
+
+    def sparse_attn(self, *a, **kw):
+        return sparse_attn(*a, _lib=self._lib, **kw)
 
     def f16_to_f64(self, bits):
         return self._lib.lid_oracle_f16_to_f64(bits)
@@ -216,6 +221,26 @@ def topk_shared(q, k, w, mask=None, kv_range=None, k_top=512, qk_dtype=None, thr
     if rc != 0:
         raise RuntimeError(f"lid_oracle_topk_shared failed: {rc}")
     return idx, score, maxabs.value
+
+
+def sparse_attn(qa, kv, idx, scale, qk_dtype=None, threads=0, _lib=None):
+    """Oracle sparse attention over the selected latent rows: o [n_tok, H, L]
+    float64 = softmax(scale * qa . kv[idx]) . kv[idx] per (query, head); idx
+    entries outside [0, n_kv) are skipped (none valid: o = 0)."""
+    dt = _dtype_of(qa, qk_dtype)
+    qa = np.ascontiguousarray(qa)
+    kv = np.ascontiguousarray(kv)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    n_tok, H, L = qa.shape
+    n_kv = kv.shape[0]
+    k_sel = idx.shape[1] if idx.ndim == 2 else 0
+    out = np.empty((n_tok, H, L), dtype=np.float64)
+    lib = _lib or _load()
+    rc = lib.lid_oracle_sparse_attn(n_tok, n_kv, H, L, k_sel, DTYPE_CODE[dt], _ptr(qa), _ptr(kv), _ptr(idx),
+                                    float(scale), _ptr(out), threads)
+    if rc != 0:
+        raise RuntimeError(f"lid_oracle_sparse_attn failed: {rc}")
+    return out
 
 
 def f16_to_f64(bits: int) -> float:

@@ -443,3 +443,76 @@ int lid_oracle_topk_shared(int64_t n_tok, int64_t n_kv, int32_t H, int32_t D, in
     if (maxabs_out) *maxabs_out = maxabs;
     return err;
 }
+
+/*
+ * Sparse attention over the selected keys (the consumer of the top-k).
+ * Issue 25468, "Root cause" comment: each CSA layer's score chain ends in a
+ * per-token top-512 selection of the compressed KV rows; ggml-org llama.cpp
+ * PR 22378, the flash-attention unblock commit: V4's MLA latent KV has K
+ * width 512, and attention is Q K^T -> softmax -> * V, where masked (-inf)
+ * slots contribute nothing.  Reading (the pages give no other attention
+ * shape): the absorbed-MLA form, in which one latent row of width L serves
+ * as both key and value, so for query t and head h
+ *     s_j    = scale * sum_d qa[t,h,d] * kv[idx[t,j], d]
+ *     o[t,h] = sum_j exp(s_j - max_j s) kv[idx[t,j]] / sum_j exp(s_j - max_j s)
+ * over the entries j of the selection with 0 <= idx[t,j] < n_kv (others,
+ * such as the top-k's -1 padding, are skipped; a repeated index counts each
+ * time); a selection with no valid entry gives o = 0.  In double throughout.
+ *   qa [n_tok, H, L], kv [n_kv, L] (dtype), idx [n_tok, k_sel] int32,
+ *   out [n_tok, H, L] double.
+ */
+int lid_oracle_sparse_attn(int64_t n_tok, int64_t n_kv, int32_t H, int32_t L, int32_t k_sel, int32_t dtype,
+                           const void* qa, const void* kv, const int32_t* idx, double scale, double* out,
+                           int32_t n_threads)
+{
+    if (n_tok < 0 || n_kv < 0 || H <= 0 || L <= 0 || k_sel < 0 || !out)
+        return ORC_EINVAL;
+    if (dtype != ORC_F32 && dtype != ORC_F16 && dtype != ORC_BF16)
+        return ORC_EINVAL;
+    if ((n_tok > 0 && (!qa || (k_sel > 0 && !idx))) || (n_kv > 0 && !kv))
+        return ORC_EINVAL;
+    double* kd = decode_keys(kv, dtype, n_kv, L, NULL);
+    if (!kd) return ORC_ENOMEM;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : err)
+    for (int64_t th = 0; th < n_tok * H; ++th) {
+        const int64_t t = th / H;
+        double* q = (double*)malloc(sizeof(double) * (size_t)L);
+        double* s = (double*)malloc(sizeof(double) * (size_t)(k_sel > 0 ? k_sel : 1));
+        if (!q || !s) { err = ORC_ENOMEM; free(q); free(s); continue; }
+        for (int32_t d = 0; d < L; ++d)
+            q[d] = decode(qa, dtype, th * L + d);
+        double mx = -INFINITY;
+        for (int32_t j = 0; j < k_sel; ++j) {
+            const int32_t r = idx[t * k_sel + j];
+            if (r < 0 || r >= n_kv) { s[j] = -INFINITY; continue; }
+            double dot = 0.0;
+            for (int32_t d = 0; d < L; ++d)
+                dot += q[d] * kd[(int64_t)r * L + d];
+            s[j] = scale * dot;
+            if (s[j] > mx) mx = s[j];
+        }
+        double* o = out + th * L;
+        for (int32_t d = 0; d < L; ++d) o[d] = 0.0;
+        if (mx > -INFINITY) {
+            double den = 0.0;
+            for (int32_t j = 0; j < k_sel; ++j) {
+                if (s[j] == -INFINITY) continue;
+                const double p = exp(s[j] - mx);
+                const int32_t r = idx[t * k_sel + j];
+                den += p;
+                for (int32_t d = 0; d < L; ++d)
+                    o[d] += p * kd[(int64_t)r * L + d];
+            }
+            for (int32_t d = 0; d < L; ++d) o[d] /= den;
+        }
+        free(q); free(s);
+    }
+    free(kd);
+    return err;
+}

@@ -456,3 +456,67 @@ def test_shared_minus_inf_term_excludes_key(oracle_lib):
     assert len(chosen) == 29 and idx[29:].tolist() == [-1] * 6 and np.all(sc[29:] == -np.inf)
     i0, s0, _ = oracle_lib.topk_shared(q[:0], k, w[:0], k_top=4)
     assert i0.tolist() == [0, 1, 2, 3] and s0.tolist() == [0.0] * 4
+
+
+# ---------------------------------------------------------------- sparse attention over the selection
+
+def _attn_brute(qa, kv, idx, scale):
+    """Python-loop softmax attention over the selected rows (math.exp, no numpy reductions)."""
+    n_tok, H, L = qa.shape
+    out = np.zeros((n_tok, H, L))
+    for t in range(n_tok):
+        rows = [int(r) for r in idx[t] if 0 <= r < kv.shape[0]]
+        for h in range(H):
+            if not rows:
+                continue
+            s = [scale * sum(float(qa[t, h, d]) * float(kv[r, d]) for d in range(L)) for r in rows]
+            mx = max(s)
+            p = [math.exp(x - mx) for x in s]
+            den = sum(p)
+            for d in range(L):
+                out[t, h, d] = sum(pj * float(kv[r, d]) for pj, r in zip(p, rows)) / den
+    return out
+
+
+def test_attn_bruteforce(oracle_lib):
+    """Random f16 inputs with padding (-1) and an out-of-range index in the
+    selection: the oracle equals a plain Python-loop softmax attention."""
+    rng = np.random.default_rng(31)
+    n_tok, n_kv, H, L, k_sel = 3, 40, 2, 6, 7
+    qa = rng.standard_normal((n_tok, H, L)).astype(np.float16)
+    kv = rng.standard_normal((n_kv, L)).astype(np.float16)
+    idx = rng.integers(0, n_kv, (n_tok, k_sel)).astype(np.int32)
+    idx[1, 3:] = -1
+    idx[2, 0] = n_kv + 5
+    out = oracle_lib.sparse_attn(qa, kv, idx, 0.7)
+    np.testing.assert_allclose(out, _attn_brute(qa, kv, idx, 0.7), rtol=1e-12, atol=1e-12)
+
+
+def test_attn_closed_forms(oracle_lib):
+    """One valid selected row: the output is that row; q = 0: the mean of the
+    selected rows (a repeated index counts twice); no valid row: 0."""
+    rng = np.random.default_rng(32)
+    n_kv, H, L = 30, 3, 16
+    kv = rng.integers(-4, 5, (n_kv, L)).astype(np.float16)
+    qa = rng.standard_normal((3, H, L)).astype(np.float16)
+    idx = np.array([[7, -1, -1, -1], [3, 5, 5, 9], [-1, -1, 40, -2]], np.int32)
+    qa[1] = 0
+    out = oracle_lib.sparse_attn(qa, kv, idx, 1.0)
+    kvd = kv.astype(np.float64)
+    assert np.array_equal(out[0], np.broadcast_to(kvd[7], (H, L)))
+    assert np.allclose(out[1], np.broadcast_to((kvd[3] + 2 * kvd[5] + kvd[9]) / 4, (H, L)), rtol=0, atol=1e-15)
+    assert np.all(out[2] == 0)
+
+
+def test_attn_permutation_and_scale(oracle_lib):
+    """Permuting a query's selection leaves its output unchanged; scaling q
+    by c equals scaling the softmax temperature by c."""
+    rng = np.random.default_rng(33)
+    qa = rng.standard_normal((2, 2, 8)).astype(np.float32)
+    kv = rng.standard_normal((50, 8)).astype(np.float32)
+    idx = rng.permutation(50)[:12].reshape(1, 12).repeat(2, axis=0).astype(np.int32)
+    a = oracle_lib.sparse_attn(qa, kv, idx, 0.5)
+    b = oracle_lib.sparse_attn(qa, kv, idx[:, ::-1].copy(), 0.5)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+    c = oracle_lib.sparse_attn((qa * 2).astype(np.float32), kv, idx, 0.25)
+    np.testing.assert_allclose(a, c, rtol=1e-13, atol=1e-13)

@@ -46,6 +46,11 @@ MUTATIONS = {
     "shared_w_of_first_query": ("double I = head_reduced_score(qd + t * H * D, wd + t * H, kd + s * D, H, D);",
                                 "double I = head_reduced_score(qd + t * H * D, wd, kd + s * D, H, D);"),
     "shared_max_not_sum": ("U += (double)v;", "U = U > (double)v ? U : (double)v;"),
+    "attn_no_scale": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "attn_not_normalised": ("for (int32_t d = 0; d < L; ++d) o[d] /= den;", "(void)den;"),
+    "attn_first_row_only": ("for (int32_t j = 0; j < k_sel; ++j) {\n                if (s[j] == -INFINITY) continue;",
+                            "for (int32_t j = 0; j < 1; ++j) {\n                if (s[j] == -INFINITY) continue;"),
+    "attn_no_max_shift": ("const double p = exp(s[j] - mx);", "const double p = exp(s[j] - 0.5 * mx);"),
 }
 
 PINS = [
@@ -65,6 +70,9 @@ PINS = [
     T.test_shared_one_query_is_per_query_topk,
     T.test_shared_identical_queries_scale,
     T.test_shared_minus_inf_term_excludes_key,
+    T.test_attn_bruteforce,
+    T.test_attn_closed_forms,
+    T.test_attn_permutation_and_scale,
 ]
 
 
