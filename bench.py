@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "indexer scored (query,key) pairs/sec + top-k tokens/sec; % MFMA / % HBM peak"
 PEAK_HBM_BPS = 8.0e12        # MI355X HBM3E, published
 PEAK_MFMA_F16 = 2.5e15       # MI355X dense f16/bf16 MFMA, published
+PEAK_F32_VALU = 157.3e12     # MI355X fp32 vector, published (256 CUs x 2.4 GHz x 256 flops per CU-clock)
 DEFAULT_STEPS = {"c2": 2000, "dec1m": 300, "c3": 400, "c4": 40, "c5": 20}
 DEFAULT_FORM = {"c2": "none", "dec1m": "none", "c3": "mask", "c4": "mask", "c5": "ranges"}
 DESCRIPTION = {
@@ -52,6 +53,7 @@ PLAN_SOURCES = {
     "prefill": ["k_prefill.hip", "lid_device.h", "lid_kernels.h"],
     "generic": ["k_generic.hip", "lid_device.h", "lid_kernels.h"],
     "shared": ["k_shared.hip", "lid_device.h", "lid_kernels.h", "lid_select.h"],
+    "attn": ["k_attn.hip", "lid_device.h", "lid_kernels.h"],
 }
 
 
@@ -148,6 +150,145 @@ def cpu_baseline(d, form, seconds, rows_hint=None):
             "sample": f"{len(rows)} of {wl.n_tok} queries (evenly spaced) with all their visible keys, {t:.1f} s"}
 
 
+# sparse-attention consumer: the prefill ubatch's shape (512 queries over
+# 16384 keys, 512 selected per query) with a synthetic attention shape (64
+# heads, latent rows of 512, bf16): the pages fix only the latent width
+ATTN_SHAPE = {"n_tok": 512, "n_kv": 16384, "n_head": 64, "latent_dim": 512, "k_sel": 512, "dtype": "bf16"}
+
+
+def bench_attn(args):
+    """Time lid_sparse_attn (one kernel per call) on ATTN_SHAPE."""
+    import numpy as np
+    import torch
+
+    import lid_inputs as li
+    import sparse_attention_token_lid_amd as L
+
+    c = ATTN_SHAPE
+    n_tok, n_kv, H, Ld, k_sel = c["n_tok"], c["n_kv"], c["n_head"], c["latent_dim"], c["k_sel"]
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else max(3, steps // 10)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = L.load()
+    log("[bench] generating the sparse-attention inputs")
+    qa_h, kv_h = li.draw_attn(n_tok, n_kv, H, Ld, c["dtype"], seed=21)
+    idx_h = li.draw_selection(n_tok, n_kv, k_sel, seed=22)
+    scale = 1.0 / math.sqrt(Ld)
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    qa0, kv0, idx0 = bf(qa_h), bf(kv_h), torch.from_numpy(idx_h).to(dev)
+    per_copy = sum(t.numel() * t.element_size() for t in (qa0, kv0, idx0))
+    copies = max(1, min(64, math.ceil((1 << 30) / per_copy)))
+    sets = [(qa0, kv0, idx0)] + [tuple(t.clone() for t in (qa0, kv0, idx0)) for _ in range(copies - 1)]
+    out = torch.empty((n_tok, H, Ld), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    calls = [(n_tok, n_kv, H, Ld, k_sel, L.LID_BF16, a.data_ptr(), b.data_ptr(), i.data_ptr(), scale,
+              out.data_ptr()) for (a, b, i) in sets]
+    log(f"[bench] mode=attn copies={copies} ({per_copy / 2**20:.1f} MiB each) steps={steps} warmup={warmup}")
+
+    def step(i, st=stream):
+        rc = lib.lid_sparse_attn(*calls[i % copies], st)
+        if rc != 0:
+            raise L.LidError(rc, "lid_sparse_attn")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    hip = L.hip_runtime()
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2 * steps):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        L.set_profile_events(evs[2 * i], evs[2 * i + 1])
+        step(i)
+    torch.cuda.synchronize()
+    L.set_profile_events(None, None)
+    kern = []
+    for i in range(steps):
+        f = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(f), evs[2 * i], evs[2 * i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        kern.append(f.value)
+    for e in evs:
+        hip.hipEventDestroy(e)
+    event_ms = sum(kern) / len(kern)
+    # timed steps: replayed from a HIP graph, G calls per graph
+    G = max(g for g in range(1, min(steps, 64) + 1) if steps % g == 0)
+    cap = torch.cuda.Stream(dev)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        s_cap = torch.cuda.current_stream(dev).cuda_stream
+        for i in range(G):
+            step(i, s_cap)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(steps // G):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    total_ms = g0.elapsed_time(g1)
+    ms_per_step = total_ms / steps
+    log(f"[bench] attn graph: {steps} steps: {total_ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step "
+        f"(event pairs {event_ms * 1e3:.2f} us)")
+    assert bool(torch.isfinite(out).all()), "non-finite attention output"
+    del graph
+    kern_ms = min(event_ms, ms_per_step)   # one kernel per call: the replay is back-to-back launches
+    # per (query, head, selected key): 2 L flops for the score, 2 L for the
+    # weighted sum (the plain definition; the kernel's split of the weights
+    # into two 16-bit parts makes its MFMA work 1.5 times this).  Latent width
+    # 512 runs on MFMA (bf16 dense peak); other widths on the fp32 vector ALU.
+    flops = 4.0 * n_tok * H * k_sel * Ld
+    achieved = flops / (kern_ms * 1e-3)
+    mfma = Ld == 512
+    pairs = n_tok * k_sel
+    res = {
+        "metric": "sparse attention (query, selected key) pairs/sec; % MFMA peak",
+        "value": pairs * steps / (total_ms * 1e-3), "unit": "pairs/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"sparse attention: n_tok {n_tok} x {k_sel} selected of n_kv {n_kv}, "
+                               f"{H} heads, latent {Ld}",
+                   **c, "parallelism": "single GPU", "mode": "attn"},
+        "timing": "HIP-graph replay of the timed steps",
+        "kernel_us": kern_ms * 1e3, "kernel_event_us": event_ms * 1e3,
+        "kernel_hash": kernel_source_hash("attn"),
+        "roofline": {"bound": "mfma" if mfma else "alu", "achieved": achieved / 1e12,
+                     "peak": (PEAK_MFMA_F16 if mfma else PEAK_F32_VALU) / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / (PEAK_MFMA_F16 if mfma else PEAK_F32_VALU), "traffic": None,
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_flops": flops},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        m = max(1, min(n_tok, threads))
+        t0 = time.perf_counter()
+        oracle.sparse_attn(qa_h[:m], kv_h, idx_h[:m], scale, qk_dtype="bf16", threads=threads)
+        t = time.perf_counter() - t0
+        if t < args.cpu_seconds / 3:
+            m = max(1, min(n_tok, int(m * args.cpu_seconds / max(t, 1e-3))))
+            t0 = time.perf_counter()
+            oracle.sparse_attn(qa_h[:m], kv_h, idx_h[:m], scale, qk_dtype="bf16", threads=threads)
+            t = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": m * k_sel / t, "unit": "pairs/s", "cores": min(threads, m * H),
+                               "kind": "oracle", "sample": f"the first {m} of {n_tok} queries, {t:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,9 +300,10 @@ def main():
     ap.add_argument("--qk", default="f16", choices=["f16", "fp8"],
                     help="f16: the workload's f16 q and k (the default); fp8: the same values quantised to "
                          "OCP E4M3 with per-row scales (max |row| / 448), run through lid_topk_fp8")
-    ap.add_argument("--mode", default="topk", choices=["topk", "scores", "shared"],
+    ap.add_argument("--mode", default="topk", choices=["topk", "scores", "shared", "attn"],
                     help="topk: the fused top-k (the default); scores: the score-only mode (lid_scores), "
-                         "which writes the n_tok x n_kv f32 scores")
+                         "which writes the n_tok x n_kv f32 scores; shared: the per-ubatch top-k "
+                         "(lid_topk_shared); attn: the sparse attention over a selection (lid_sparse_attn)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -175,6 +317,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+
+    if args.mode == "attn":
+        bench_attn(args)
         return
 
     import numpy as np

@@ -184,6 +184,33 @@ int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const 
                     const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Sparse attention over the selected keys: the consumer of the top-k.  For
+ * query t and head h, over the entries j of idx[t,:] with 0 <= idx[t,j] <
+ * n_kv (others, such as lid_topk's -1 padding, are skipped; a repeated index
+ * counts once per entry):
+ *   s_j    = scale * sum_d qa[t,h,d] * kv[idx[t,j], d]
+ *   out[t,h,:] = sum_j softmax_j(s) * kv[idx[t,j], :]     (0 if no entry is valid)
+ * Issue 25468, "Root cause" comment: each CSA layer's top-512 selection of
+ * the compressed KV rows feeds that layer's attention; ggml-org llama.cpp PR
+ * 22378, the flash-attention unblock commit: the MLA latent KV row is 512
+ * wide and attention is softmax(Q K^T) V.  The absorbed-MLA form is read: one
+ * latent row serves as key and as value (the query has been multiplied into
+ * the latent space beforehand by the caller).
+ *   qa    [n_tok, n_head, latent_dim]  qk_dtype (LID_F16 or LID_BF16)
+ *   kv    [n_kv, latent_dim]           qk_dtype
+ *   idx   [n_tok, k_sel]               int32 (any values; out of range = skipped)
+ *   out   [n_tok, n_head, latent_dim]  f32 output
+ * All device pointers, caller-owned, contiguous; qa, kv and out 16-byte
+ * aligned.  8 <= latent_dim <= 1024 with latent_dim % 8 == 0 (larger:
+ * LID_ERR_UNSUPPORTED); k_sel >= 0; scale finite (1/sqrt(latent_dim) for the
+ * usual scaling: not implied).  Scores, the running maximum, the softmax
+ * denominator and the weighted sum are f32.  Asynchronous on `stream`, no
+ * workspace, deterministic; errors as for lid_topk.  The profile events of
+ * lid_set_profile_events bracket its one kernel. */
+int lid_sparse_attn(int64_t n_tok, int64_t n_kv, int32_t n_head, int32_t latent_dim, int32_t k_sel,
+                    int32_t qk_dtype, const void* qa, const void* kv, const int32_t* idx, float scale,
+                    float* out, void* stream);
+
 /* The plan lid_topk would run for `shape` (a lid_plan value), and through
  * `splits_out` (may be NULL) its key splits per query; negative lid_status if
  * the shape is invalid or unsupported. */

@@ -88,6 +88,24 @@ def draw_qkw(n_tok, n_kv, n_head, head_dim, dtype="f16", w_div_h=True, seed=0):
     return _round_qk(q, dtype), _round_qk(k, dtype), np.ascontiguousarray(w, dtype=np.float32)
 
 
+def draw_attn(n_tok, n_kv, n_head, latent_dim, dtype="f16", seed=0):
+    """Sparse-attention operands: qa [n_tok,H,L] and kv [n_kv,L], standard
+    normal, in the storage dtype (bf16 as uint16 bit patterns)."""
+    rng = np.random.default_rng(seed)
+    qa = rng.standard_normal((n_tok, n_head, latent_dim), dtype=np.float32)
+    kv = rng.standard_normal((n_kv, latent_dim), dtype=np.float32)
+    return _round_qk(qa, dtype), _round_qk(kv, dtype)
+
+
+def draw_selection(n_tok, n_kv, k_sel, seed=0):
+    """int32 [n_tok, k_sel]: k_sel distinct random keys per query (any order),
+    the shape of a full top-k selection."""
+    rng = np.random.default_rng(seed)
+    if k_sel > n_kv:
+        raise ValueError("k_sel > n_kv")
+    return np.argsort(rng.random((n_tok, n_kv), dtype=np.float32), axis=1)[:, :k_sel].astype(np.int32)
+
+
 def visible_ranges(wl: Workload) -> np.ndarray | None:
     """Per-query half-open visible key range [lo, hi) as int32 [n_tok, 2], or None.
 

@@ -28,7 +28,7 @@ PLAN_NAMES = {PLAN_GENERIC: "generic", PLAN_PREFILL: "prefill", PLAN_DECODE: "de
 STATUS = {0: "LID_OK", -1: "LID_ERR_INVALID_ARG", -2: "LID_ERR_UNSUPPORTED", -3: "LID_ERR_WORKSPACE",
           -4: "LID_ERR_HIP"}
 EXPORTS = ("lid_topk", "lid_topk_fp8", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores",
-           "lid_topk_shared", "lid_topk_shared_workspace_size",
+           "lid_topk_shared", "lid_topk_shared_workspace_size", "lid_sparse_attn",
            "lid_status_string", "lid_last_hip_error", "lid_set_profile_events", "lid_version")
 
 
@@ -77,6 +77,9 @@ def load():
         lib.lid_topk_shared.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lid_topk_shared_workspace_size.restype = ctypes.c_size_t
         lib.lid_topk_shared_workspace_size.argtypes = [ctypes.POINTER(LidShape)]
+        lib.lid_sparse_attn.restype = ctypes.c_int
+        lib.lid_sparse_attn.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, vp, vp, vp, ctypes.c_float, vp, vp]
         lib.lid_topk_plan.restype = ctypes.c_int
         lib.lid_topk_plan.argtypes = [ctypes.POINTER(LidShape), ctypes.POINTER(ctypes.c_int32)]
         lib.lid_status_string.restype = ctypes.c_char_p
@@ -217,6 +220,35 @@ def topk_shared(q, k, w, mask=None, kv_range=None, k_top=512, *, idx=None, score
     if rc != 0:
         raise LidError(rc)
     return idx, score
+
+
+def sparse_attn(qa, kv, idx, scale, *, out=None, stream=None):
+    """Sparse attention over the selected latent rows (lid_sparse_attn):
+    out [n_tok, H, L] f32 = softmax(scale * qa . kv[idx]) . kv[idx] per
+    (query, head), over the entries of idx [n_tok, k_sel] inside [0, n_kv)."""
+    import torch
+    if qa.dim() != 3 or kv.dim() != 2 or idx.dim() != 2:
+        raise ValueError("qa [n_tok,H,L], kv [n_kv,L], idx [n_tok,k_sel] expected")
+    n_tok, H, L = qa.shape
+    dev = qa.device
+    if dev.type != "cuda":
+        raise ValueError("lid.sparse_attn runs on the GPU only (qa is on %s)" % dev)
+    for name, t in (("qa", qa), ("kv", kv), ("idx", idx)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if kv.dtype != qa.dtype or kv.shape[1] != L or idx.shape[0] != n_tok or idx.dtype != torch.int32:
+        raise ValueError("dtype/shape mismatch among qa, kv, idx")
+    if out is None:
+        out = torch.empty((n_tok, H, L), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (n_tok, H, L) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [n_tok, H, L] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = load().lid_sparse_attn(n_tok, kv.shape[0], H, L, idx.shape[1], _dtype_code(qa), _ptr(qa), _ptr(kv),
+                                _ptr(idx), float(scale), _ptr(out), stream)
+    if rc != 0:
+        raise LidError(rc)
+    return out
 
 
 def scores(q, k, w, mask=None, kv_range=None, *, out=None, stream=None):

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblid.so")
 SOURCES = ["lid_api.hip", "k_prefill.hip", "k_decode.hip", "k_merge.hip", "k_generic.hip", "k_scores.hip",
-           "k_shared.hip"]
+           "k_shared.hip", "k_attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

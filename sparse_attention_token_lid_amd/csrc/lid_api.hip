@@ -423,6 +423,34 @@ int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const 
   return LID_OK;
 }
 
+int lid_sparse_attn(int64_t n_tok, int64_t n_kv, int32_t n_head, int32_t latent_dim, int32_t k_sel,
+                    int32_t qk_dtype, const void* qa, const void* kv, const int32_t* idx, float scale, float* out,
+                    void* stream) {
+  if (n_tok < 0 || n_kv < 0 || n_kv > INT32_MAX || n_head < 1 || latent_dim < 8 || k_sel < 0)
+    return LID_ERR_INVALID_ARG;
+  if (latent_dim % 8 != 0 || !(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return LID_ERR_INVALID_ARG;
+  if (qk_dtype != LID_F16 && qk_dtype != LID_BF16) return LID_ERR_UNSUPPORTED;
+  if (latent_dim > 1024) return LID_ERR_UNSUPPORTED;
+  if (n_tok == 0) return LID_OK;
+  // one 256-lane workgroup per query and 4 heads: the grid's lane count must fit 32 bits
+  if (n_tok * (int64_t)((n_head + 3) / 4) > (int64_t)(1u << 24) - 1) return LID_ERR_UNSUPPORTED;
+  if (!qa || !out || (k_sel > 0 && !idx) || (n_kv > 0 && k_sel > 0 && !kv)) return LID_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(qa) & 15) || (reinterpret_cast<uintptr_t>(kv) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15) || (reinterpret_cast<uintptr_t>(idx) & 3))
+    return LID_ERR_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // with no keys every entry is invalid: the result is that of an empty selection
+  const int ks = n_kv == 0 ? 0 : k_sel;
+  hipError_t e;
+  if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
+  if ((e = launch_sparse_attn(qa, kv, idx, out, n_tok, n_kv, n_head, latent_dim, ks, qk_dtype, scale, st)) !=
+      hipSuccess)
+    return hip_fail(e);
+  if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
+  return LID_OK;
+}
+
 const char* lid_status_string(int status) {
   switch (status) {
     case LID_OK: return "ok";

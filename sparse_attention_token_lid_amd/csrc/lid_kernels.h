@@ -67,6 +67,10 @@ size_t shared_lists_lds_bytes(int K);
 hipError_t launch_shared_merge(const KArgs& a, int ch, hipStream_t st);  // a.P lists of a.K -> the output row
 size_t shared_merge_lds_bytes(int P, int K, int ch);
 
+// sparse attention over the selected latent rows (dtype: 1 f16, 2 bf16; L <= 1024, L % 8 == 0)
+hipError_t launch_sparse_attn(const void* qa, const void* kv, const int32_t* idx, float* out, int64_t n_tok,
+                              int64_t n_kv, int H, int L, int k_sel, int dtype, float scale, hipStream_t st);
+
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st);
 size_t merge_lds_bytes(int P, int K, int ch);
 
