@@ -151,23 +151,29 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 //
 // One workgroup of 4 wavefronts per (query t, tile of 64 heads); wavefront w
 // owns heads 16 w .. 16 w + 15 of the tile.  The selection is walked in
-// blocks of 32 entries: each block's rows are gathered from HBM (wavefront w
-// loads rows 8 w .. 8 w + 7, 1 KiB per row per instruction) into registers
-// while the block before is scored, and written to the other of two LDS
-// buffers (row-major, row pitch 1040 B) before that block's weighted sum.  Per block and wavefront, with v_mfma_f32_16x16x32:
-//   S^T (32 keys x 16 heads) = K_blk Q^T: A = the key rows from LDS (16 B
-//       per lane), B = this wavefront's q rows, held in registers for the
-//       whole walk (16 k-steps of 32 dims);
-//   online softmax in f32: lane l has heads l % 16 and keys 4 (l / 16) + i
-//       and 16 + 4 (l / 16) + i of the block, so a head's maximum and sum
-//       are two cross-lane steps; the running maximum is only moved when the
-//       block's maximum exceeds it by more than 8 (weights up to e^8 stay
-//       exact in f32), so the accumulator is rarely rescaled;
-//   O^T (512 dims x 16 heads) += K_blk^T P^T: A = the key rows read by
-//       column from LDS (8 x 2 B per lane), B = the weights.  The MFMA's
-//       k-slot 8 (l / 16) + j is mapped to the key the lane already holds
-//       (4 (l / 16) + j, then 16 + 4 (l / 16) + j - 4), so P^T never leaves
-//       the registers; the sum over k is order-free, and A uses the same map.
+// blocks of 32 entries.  Per block and wavefront, with v_mfma_f32_16x16x32:
+//   S^T (32 keys x 16 heads) = K_blk Q^T: A = key rows (16 B per lane) from
+//       a row-major LDS copy of the block, B = this wavefront's q rows, held
+//       in registers for the whole walk (16 k-steps of 32 dims);
+//   online softmax in f32: lane l has head l % 16 and the block's keys
+//       4 (l / 16) + i and 16 + 4 (l / 16) + i (i < 4), so a head's maximum
+//       and sum are two cross-lane steps; the running maximum is only moved
+//       when the block's maximum exceeds it by more than 8 (weights up to e^8
+//       stay exact in f32), so the accumulator is rarely rescaled;
+//   O^T (512 dims x 16 heads) += K_blk^T P^T: the MFMA's k-slot
+//       8 (l / 16) + j is the key the lane already holds (4 (l / 16) + j, then
+//       16 + 4 (l / 16) + j - 4), so P^T never leaves the registers (the sum
+//       over k is order-free); A comes from a second, transposed LDS copy of
+//       the block whose rows (one per latent dim) list the keys in that
+//       order, so each A fragment is one 16-byte read.
+// Gathering: wavefront w loads the rows of keys 4 w .. 4 w + 3 and
+// 16 + 4 w .. 16 + 4 w + 3 (1 KiB per row per instruction), which are
+// exactly the 8 keys of one 16-byte chunk of the transposed rows, into
+// registers while the block before is processed, and writes both LDS copies
+// (double-buffered) after it.  The transposed rows
+// (80 B pitch) swizzle their four chunks by (dim / 8) mod 4 so that both the
+// writes (lanes 8 dims apart) and the reads (16 consecutive dims) spread
+// over the banks.
 // The weights are split into two 16-bit parts, p = hi + lo (lo = the
 // rounding residual of hi), and both are multiplied in, so the weighted sum
 // keeps about 16 bits of each weight instead of the 8 of a single bf16; the
@@ -176,7 +182,8 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 
 constexpr int kAL = 512;               // latent width of this path
 constexpr int kAKB = 32;               // selection entries per block
-constexpr int kAPitch = kAL + 8;       // LDS row pitch in 16-bit elements (1040 B)
+constexpr int kAPitch = kAL + 8;       // row-major copy: row pitch in 16-bit elements (1040 B)
+constexpr int kATPitch = 40;           // transposed copy: row pitch in 16-bit elements (80 B)
 constexpr int kANks = kAL / 32;        // k-steps of S^T
 constexpr int kANdt = kAL / 16;        // 16-dim tiles of O^T
 constexpr float kAMaxSlack = 8.f;
@@ -211,6 +218,9 @@ template <> struct AMfma<2> {
   static __device__ __forceinline__ float from16(uint32_t b) { return __uint_as_float(b << 16); }
 };
 
+// block key of k-slot j (0..7) of lane group g (0..3)
+__device__ __forceinline__ int attn_key(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
+
 template <int DT>
 __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t* __restrict__ qa,
                                                                   const uint16_t* __restrict__ kv,
@@ -219,11 +229,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
                                                                   int k_sel, float scale) {
   typedef AMfma<DT> M;
   typedef typename M::T T;
-  __shared__ __align__(16) uint16_t krow[2][kAKB][kAPitch];
+  __shared__ __align__(16) uint16_t krow[2][kAKB][kAPitch];   // [buf][key][dim]
+  __shared__ __align__(16) uint16_t kt[2][kAL][kATPitch];     // [buf][dim][key, in k-slot order, swizzled]
   __shared__ __align__(4) uint8_t vflag[2][kAKB];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int g = lane >> 4, r = lane & 15;
   const int nht = (H + 63) / 64;
   const int64_t t = blockIdx.x / nht;
@@ -244,31 +255,46 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
 
   const int32_t* irow = idx + t * (int64_t)k_sel;
   const int nb = (k_sel + kAKB - 1) / kAKB;
-  u32x4 st[8];
+  u32x4 st[8];     // rows of keys attn_key(w, i), dims 8 lane .. 8 lane + 7
   uint32_t vm = 0;
   auto fetch = [&](int b) {
     vm = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int e = b * kAKB + 8 * w + i;
-      const int32_t ri = e < k_sel ? irow[e] : -1;   // wave-uniform
+      const int e = b * kAKB + attn_key(w, i);
+      // wave-uniform; read unconditionally (clamped: k_sel >= 1 here) so that
+      // the eight loads issue back to back
+      const int32_t rr = irow[e < k_sel ? e : k_sel - 1];
+      const int32_t ri = e < k_sel ? rr : -1;
       const bool v = ri >= 0 && (int64_t)ri < n_kv;
       vm |= (uint32_t)v << i;
       const int64_t row = v ? ri : 0;
       st[i] = *reinterpret_cast<const u32x4*>(kv + row * kAL + 8 * lane);
     }
   };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&krow[buf][attn_key(w, i)][8 * lane]) = st[i];
+    // transposed: dim 8 lane + c gets the 8 keys of chunk w (swizzled by lane & 3)
+    const int chunk = w ^ (lane & 3);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int q = c >> 1;
+      uint32_t x[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const uint32_t a = st[2 * k2][q], b = st[2 * k2 + 1][q];
+        x[k2] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      }
+      *reinterpret_cast<u32x4*>(&kt[buf][8 * lane + c][8 * chunk]) = u32x4{x[0], x[1], x[2], x[3]};
+    }
+    if (lane < 8) vflag[buf][attn_key(w, lane)] = (uint8_t)((vm >> lane) & 1u);
+  };
 
   f32x4 acc[kANdt];
 #pragma unroll
   for (int d = 0; d < kANdt; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), den = 0.f;
-
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&krow[buf][8 * w + i][8 * lane]) = st[i];
-    if (lane < 8) vflag[buf][8 * w + lane] = (uint8_t)((vm >> lane) & 1u);
-  };
 
   if (nb > 0) {
     fetch(0);
@@ -277,19 +303,26 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
   for (int b = 0; b < nb; ++b) {
     const int buf = b & 1;
     // every wavefront has staged block b and finished block b - 1 (whose
-    // buffer the next block's rows go to)
+    // buffers the next block's rows go to)
     __syncthreads();
     if (b + 1 < nb) fetch(b + 1);
 
-    // S^T: keys r and 16 + r of the block (A), this wavefront's heads (B)
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // S^T: keys r and 16 + r of the block (A), this wavefront's heads (B);
+    // even and odd k-steps in separate chains
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
 #pragma unroll
-    for (int ks = 0; ks < kANks; ++ks) {
+    for (int ks = 0; ks < kANks; ks += 2) {
       const T a0 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][r][32 * ks + 8 * g]));
       const T a1 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][16 + r][32 * ks + 8 * g]));
+      const T a2 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][r][32 * ks + 32 + 8 * g]));
+      const T a3 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][16 + r][32 * ks + 32 + 8 * g]));
       s0 = M::run(a0, qf[ks], s0);
       s1 = M::run(a1, qf[ks], s1);
+      s2 = M::run(a2, qf[ks + 1], s2);
+      s3 = M::run(a3, qf[ks + 1], s3);
     }
+    s0 += s2;
+    s1 += s3;
     // lane: head r, keys 4 g + i (s0) and 16 + 4 g + i (s1)
     const uint32_t f0 = *reinterpret_cast<const uint32_t*>(&vflag[buf][4 * g]);
     const uint32_t f1 = *reinterpret_cast<const uint32_t*>(&vflag[buf][16 + 4 * g]);
@@ -326,24 +359,29 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     }
     den += ps;
     m = mn;
-    if (b + 1 < nb) stage(buf ^ 1);   // the next block's rows have had S^T's time to arrive
     const T phi = __builtin_bit_cast(T, u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
                                               hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)});
     const T plo = __builtin_bit_cast(T, u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
                                               lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)});
-    // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot j] = key row (j < 4 ? 4 g + j : 12 + 4 g + j)
-    const uint16_t* k0 = &krow[buf][4 * g][r];
-    const uint16_t* k1 = &krow[buf][16 + 4 * g][r];
+    // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot 8 g + j], one 16-byte
+    // read; the lo product of tile d - 1 is issued between the hi products of
+    // tiles d and d + 1, so no MFMA waits on the one just before it
+    auto afrag = [&](int d) {
+      const int dim = 16 * d + r;
+      const int chunk = g ^ ((dim >> 3) & 3);
+      return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&kt[buf][dim][8 * chunk]));
+    };
+    T aprev = afrag(0);
+    acc[0] = M::run(aprev, phi, acc[0]);
 #pragma unroll
-    for (int d = 0; d < kANdt; ++d) {
-      const uint32_t e0 = k0[16 * d], e1 = k0[kAPitch + 16 * d], e2 = k0[2 * kAPitch + 16 * d],
-                     e3 = k0[3 * kAPitch + 16 * d];
-      const uint32_t e4 = k1[16 * d], e5 = k1[kAPitch + 16 * d], e6 = k1[2 * kAPitch + 16 * d],
-                     e7 = k1[3 * kAPitch + 16 * d];
-      const T a = __builtin_bit_cast(T, u32x4{e0 | (e1 << 16), e2 | (e3 << 16), e4 | (e5 << 16), e6 | (e7 << 16)});
+    for (int d = 1; d < kANdt; ++d) {
+      const T a = afrag(d);
       acc[d] = M::run(a, phi, acc[d]);
-      acc[d] = M::run(a, plo, acc[d]);
+      acc[d - 1] = M::run(aprev, plo, acc[d - 1]);
+      aprev = a;
     }
+    acc[kANdt - 1] = M::run(aprev, plo, acc[kANdt - 1]);
+    if (b + 1 < nb) stage(buf ^ 1);   // the next block's rows have had this block's time to arrive
   }
   // lane: head r, dims 16 d + 4 g .. + 3
   if (hok) {
