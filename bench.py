@@ -268,7 +268,8 @@ def bench_attn(args):
         "kernel_hash": kernel_source_hash("attn"),
         "roofline": {"bound": "mfma" if mfma else "alu", "achieved": achieved / 1e12,
                      "peak": (PEAK_MFMA_F16 if mfma else PEAK_F32_VALU) / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / (PEAK_MFMA_F16 if mfma else PEAK_F32_VALU), "traffic": None,
+                     "frac": achieved / (PEAK_MFMA_F16 if mfma else PEAK_F32_VALU),
+                     "traffic": stored_traffic("attn", "attn", 1) if mfma else None,
                      "traffic_unit": "HBM bytes per launch", "algorithmic_flops": flops},
     }
     if not args.no_cpu_baseline:
