@@ -166,7 +166,8 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 //       over k is order-free); A comes from a second, transposed LDS copy of
 //       the block whose rows (one per latent dim) list the keys in that
 //       order, so each A fragment is one 16-byte read.
-// Gathering: wavefront w loads the rows of keys 4 w .. 4 w + 3 and
+// Gathering: the selection entries are read two blocks ahead, and
+// wavefront w loads the rows of keys 4 w .. 4 w + 3 and
 // 16 + 4 w .. 16 + 4 w + 3 (1 KiB per row per instruction), which are
 // exactly the 8 keys of one 16-byte chunk of the transposed rows, into
 // registers while the block before is processed, and writes both LDS copies
@@ -257,16 +258,23 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
   const int nb = (k_sel + kAKB - 1) / kAKB;
   u32x4 st[8];     // rows of keys attn_key(w, i), dims 8 lane .. 8 lane + 7
   uint32_t vm = 0;
+  // the selection entries of a block's rows, read one block ahead of the rows
+  // themselves by one vector load (lane i < 8 holds entry attn_key(w, i);
+  // clamped, so no branch: k_sel >= 1 whenever a block exists) and broadcast
+  // with readlane when the rows are fetched, so the row loads never wait on
+  // them (a scalar load would be waited for with the LDS reads)
+  int32_t ixv = 0;
+  auto load_idx = [&](int b) {
+    const int e = b * kAKB + attn_key(w, lane & 7);
+    ixv = irow[e < k_sel ? e : k_sel - 1];
+  };
   auto fetch = [&](int b) {
     vm = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int e = b * kAKB + attn_key(w, i);
-      // wave-uniform; read unconditionally (clamped: k_sel >= 1 here) so that
-      // the eight loads issue back to back
-      const int32_t rr = irow[e < k_sel ? e : k_sel - 1];
-      const int32_t ri = e < k_sel ? rr : -1;
-      const bool v = ri >= 0 && (int64_t)ri < n_kv;
+      const int32_t ri = __builtin_amdgcn_readlane(ixv, i);
+      const bool v = e < k_sel && ri >= 0 && (int64_t)ri < n_kv;
       vm |= (uint32_t)v << i;
       const int64_t row = v ? ri : 0;
       st[i] = *reinterpret_cast<const u32x4*>(kv + row * kAL + 8 * lane);
@@ -297,8 +305,10 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
   float m = -__builtin_inff(), den = 0.f;
 
   if (nb > 0) {
+    load_idx(0);
     fetch(0);
     stage(0);
+    if (nb > 1) load_idx(1);
   }
   for (int b = 0; b < nb; ++b) {
     const int buf = b & 1;
@@ -306,6 +316,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     // buffers the next block's rows go to)
     __syncthreads();
     if (b + 1 < nb) fetch(b + 1);
+    if (b + 2 < nb) load_idx(b + 2);
 
     // S^T: keys r and 16 + r of the block (A), this wavefront's heads (B);
     // even and odd k-steps in separate chains
