@@ -166,12 +166,11 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 //       over k is order-free); A comes from a second, transposed LDS copy of
 //       the block whose rows (one per latent dim) list the keys in that
 //       order, so each A fragment is one 16-byte read.
-// Gathering: the selection entries are read two blocks ahead, and
-// wavefront w loads the rows of keys 4 w .. 4 w + 3 and
+// Gathering: wavefront w loads the rows of keys 4 w .. 4 w + 3 and
 // 16 + 4 w .. 16 + 4 w + 3 (1 KiB per row per instruction), which are
 // exactly the 8 keys of one 16-byte chunk of the transposed rows, into
-// registers while the block before is processed, and writes both LDS copies
-// (double-buffered) after it.  The transposed rows
+// registers two blocks ahead (their indices three blocks ahead), and writes
+// both LDS copies (double-buffered) at the end of the block before.  The transposed rows
 // (80 B pitch) swizzle their four chunks by (dim / 8) mod 4 so that both the
 // writes (lanes 8 dims apart) and the reads (16 consecutive dims) spread
 // over the banks.
@@ -256,8 +255,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
 
   const int32_t* irow = idx + t * (int64_t)k_sel;
   const int nb = (k_sel + kAKB - 1) / kAKB;
-  u32x4 st[8];     // rows of keys attn_key(w, i), dims 8 lane .. 8 lane + 7
-  uint32_t vm = 0;
+  // a block's gathered rows in registers: keys attn_key(w, i), dims 8 lane ..
+  // 8 lane + 7, and their validity bits
+  struct Rows {
+    u32x4 st[8];
+    uint32_t vm;
+  };
   // the selection entries of a block's rows, read one block ahead of the rows
   // themselves by one vector load (lane i < 8 holds entry attn_key(w, i);
   // clamped, so no branch: k_sel >= 1 whenever a block exists) and broadcast
@@ -268,8 +271,8 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     const int e = b * kAKB + attn_key(w, lane & 7);
     ixv = irow[e < k_sel ? e : k_sel - 1];
   };
-  auto fetch = [&](int b) {
-    vm = 0;
+  auto fetch = [&](int b, Rows& R) {
+    uint32_t vm = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int e = b * kAKB + attn_key(w, i);
@@ -277,10 +280,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
       const bool v = e < k_sel && ri >= 0 && (int64_t)ri < n_kv;
       vm |= (uint32_t)v << i;
       const int64_t row = v ? ri : 0;
-      st[i] = *reinterpret_cast<const u32x4*>(kv + row * kAL + 8 * lane);
+      R.st[i] = *reinterpret_cast<const u32x4*>(kv + row * kAL + 8 * lane);
     }
+    R.vm = vm;
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, const Rows& R) {
+    const u32x4* st = R.st;
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&krow[buf][attn_key(w, i)][8 * lane]) = st[i];
     // transposed: dim 8 lane + c gets the 8 keys of chunk w (swizzled by lane & 3)
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
       }
       *reinterpret_cast<u32x4*>(&kt[buf][8 * lane + c][8 * chunk]) = u32x4{x[0], x[1], x[2], x[3]};
     }
-    if (lane < 8) vflag[buf][attn_key(w, lane)] = (uint8_t)((vm >> lane) & 1u);
+    if (lane < 8) vflag[buf][attn_key(w, lane)] = (uint8_t)((R.vm >> lane) & 1u);
   };
 
   f32x4 acc[kANdt];
@@ -304,19 +309,29 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
   for (int d = 0; d < kANdt; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), den = 0.f;
 
+  // Rows are gathered two blocks ahead, into two register sets used in turn
+  // (block j's rows in set j mod 2); the loop is unrolled by two so that the
+  // sets are fixed registers.  Indices are read one block ahead of the rows.
+  Rows ra, rb;
   if (nb > 0) {
     load_idx(0);
-    fetch(0);
-    stage(0);
-    if (nb > 1) load_idx(1);
+    fetch(0, ra);
+    stage(0, ra);
+    if (nb > 1) {
+      load_idx(1);
+      fetch(1, rb);
+      if (nb > 2) load_idx(2);
+    }
   }
-  for (int b = 0; b < nb; ++b) {
+  // one block: rcur held block b's rows (already staged) and takes block b + 2's;
+  // rnext holds block b + 1's, staged at the end
+  auto block = [&](int b, Rows& rcur, const Rows& rnext) {
     const int buf = b & 1;
     // every wavefront has staged block b and finished block b - 1 (whose
     // buffers the next block's rows go to)
     __syncthreads();
-    if (b + 1 < nb) fetch(b + 1);
-    if (b + 2 < nb) load_idx(b + 2);
+    if (b + 2 < nb) fetch(b + 2, rcur);
+    if (b + 3 < nb) load_idx(b + 3);
 
     // S^T: keys r and 16 + r of the block (A), this wavefront's heads (B);
     // even and odd k-steps in separate chains
@@ -392,7 +407,11 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
       aprev = a;
     }
     acc[kANdt - 1] = M::run(aprev, plo, acc[kANdt - 1]);
-    if (b + 1 < nb) stage(buf ^ 1);   // the next block's rows have had this block's time to arrive
+    if (b + 1 < nb) stage(buf ^ 1, rnext);   // fetched a block and a half ago
+  };
+  for (int b = 0; b < nb; b += 2) {
+    block(b, ra, rb);
+    if (b + 1 < nb) block(b + 1, rb, ra);
   }
   // lane: head r, dims 16 d + 4 g .. + 3
   if (hok) {
