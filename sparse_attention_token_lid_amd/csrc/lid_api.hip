@@ -433,8 +433,10 @@ int lid_sparse_attn(int64_t n_tok, int64_t n_kv, int32_t n_head, int32_t latent_
   if (qk_dtype != LID_F16 && qk_dtype != LID_BF16) return LID_ERR_UNSUPPORTED;
   if (latent_dim > 1024) return LID_ERR_UNSUPPORTED;
   if (n_tok == 0) return LID_OK;
-  // one 256-lane workgroup per query and 4 heads: the grid's lane count must fit 32 bits
-  if (n_tok * (int64_t)((n_head + 3) / 4) > (int64_t)(1u << 24) - 1) return LID_ERR_UNSUPPORTED;
+  // 256-lane workgroups, one per query and 64 heads (latent width 512, MFMA) or 4 heads
+  // (other widths): the grid's lane count must fit 32 bits
+  const int64_t heads_per_wg = latent_dim == 512 ? 64 : 4;
+  if (n_tok * ((n_head + heads_per_wg - 1) / heads_per_wg) > (int64_t)(1u << 24) - 1) return LID_ERR_UNSUPPORTED;
   if (!qa || !out || (k_sel > 0 && !idx) || (n_kv > 0 && k_sel > 0 && !kv)) return LID_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(qa) & 15) || (reinterpret_cast<uintptr_t>(kv) & 15) ||
       (reinterpret_cast<uintptr_t>(out) & 15) || (reinterpret_cast<uintptr_t>(idx) & 3))

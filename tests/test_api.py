@@ -181,3 +181,45 @@ def test_shared_plan_and_errors(L):
              None) == -2                                                                      # f32: no MFMA path
     assert f(ctypes.byref(shape_of("c1")), 16, 16, 16, None, None, 16, None, 16, ws, None) == -2  # H=4, D=32
     assert lib.lid_topk_shared_workspace_size(ctypes.byref(shape_of("c3", k_top=0))) == 0
+
+
+def test_sparse_attn_argument_checks(L):
+    """lid_sparse_attn: every check that runs before a launch (no GPU needed:
+    each of these returns before any HIP call)."""
+    lib = L.load()
+    f = lib.lid_sparse_attn
+    F16, BF16, F32 = L.LID_F16, L.LID_BF16, L.LID_F32
+    # (n_tok, n_kv, H, L, k_sel, dtype, qa, kv, idx, scale, out)
+    ok = (4, 100, 8, 512, 16, F16, 16, 16, 16, 1.0, 16)
+
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[["n_tok", "n_kv", "H", "L", "k_sel", "dt", "qa", "kv", "idx", "scale", "out"].index(k)] = v
+        return f(*a, None)
+
+    assert call(n_tok=0) == 0                         # nothing to do: no launch
+    assert call(n_tok=-1) == -1
+    assert call(n_kv=-1) == -1
+    assert call(n_kv=2 ** 31) == -1
+    assert call(H=0) == -1
+    assert call(L=60) == -1                           # not a multiple of 8
+    assert call(L=0) == -1
+    assert call(L=1032) == -2                         # above 1024
+    assert call(k_sel=-1) == -1
+    assert call(dt=F32) == -2
+    assert call(dt=L.LID_F8E4M3) == -2
+    assert call(scale=float("nan")) == -1
+    assert call(scale=float("inf")) == -1
+    assert call(qa=None) == -1
+    assert call(out=None) == -1
+    assert call(idx=None) == -1                       # k_sel > 0 needs the selection
+    assert call(kv=None) == -1                        # keys and a selection need kv
+    assert call(qa=8) == -1                           # misaligned
+    assert call(kv=24) == -1
+    assert call(out=4) == -1
+    assert call(idx=2) == -1
+    # the grid's lane count must fit 32 bits: 64 heads per workgroup at width 512, 4 otherwise
+    assert call(n_tok=1 << 24, H=64, L=256) == -2
+    assert call(n_tok=1 << 24, H=64, L=512) == -2
+    assert call(n_tok=(1 << 24) - 1, H=64, L=512, qa=None) == -1   # fits: reaches the pointer checks
