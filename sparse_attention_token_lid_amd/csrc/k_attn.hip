@@ -169,8 +169,10 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 // Gathering: wavefront w loads the rows of keys 4 w .. 4 w + 3 and
 // 16 + 4 w .. 16 + 4 w + 3 (1 KiB per row per instruction), which are
 // exactly the 8 keys of one 16-byte chunk of the transposed rows, into
-// registers two blocks ahead (their indices three blocks ahead), and writes
-// both LDS copies (double-buffered) at the end of the block before.  The transposed rows
+// registers three blocks ahead (their indices four blocks ahead), and writes
+// both LDS copies (double-buffered) two blocks ahead.  The blocks are
+// software-pipelined: block b + 1's S^T and softmax run beside block b's
+// weighted sum.  The transposed rows
 // (80 B pitch) swizzle their four chunks by (dim / 8) mod 4 so that both the
 // writes (lanes 8 dims apart) and the reads (16 consecutive dims) spread
 // over the banks.
@@ -309,33 +311,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
   for (int d = 0; d < kANdt; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), den = 0.f;
 
-  // Rows are gathered two blocks ahead, into two register sets used in turn
-  // (block j's rows in set j mod 2); the loop is unrolled by two so that the
-  // sets are fixed registers.  Indices are read one block ahead of the rows.
-  Rows ra, rb;
-  if (nb > 0) {
-    load_idx(0);
-    fetch(0, ra);
-    stage(0, ra);
-    if (nb > 1) {
-      load_idx(1);
-      fetch(1, rb);
-      if (nb > 2) load_idx(2);
-    }
-  }
-  // one block: rcur held block b's rows (already staged) and takes block b + 2's;
-  // rnext holds block b + 1's, staged at the end
-  auto block = [&](int b, Rows& rcur, const Rows& rnext) {
-    const int buf = b & 1;
-    // every wavefront has staged block b and finished block b - 1 (whose
-    // buffers the next block's rows go to)
-    __syncthreads();
-    if (b + 2 < nb) fetch(b + 2, rcur);
-    if (b + 3 < nb) load_idx(b + 3);
-
-    // S^T: keys r and 16 + r of the block (A), this wavefront's heads (B);
-    // even and odd k-steps in separate chains
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, s2 = s0, s3 = s0;
+  // S^T of a staged block: lane gets head r and keys 4 g + i (s0), 16 + 4 g + i
+  // (s1); even and odd k-steps in separate chains
+  auto scores = [&](int buf, f32x4& s0, f32x4& s1) {
+    f32x4 s2 = {0.f, 0.f, 0.f, 0.f}, s3 = s2;
+    s0 = s2;
+    s1 = s2;
 #pragma unroll
     for (int ks = 0; ks < kANks; ks += 2) {
       const T a0 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][r][32 * ks + 8 * g]));
@@ -349,7 +330,11 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     }
     s0 += s2;
     s1 += s3;
-    // lane: head r, keys 4 g + i (s0) and 16 + 4 g + i (s1)
+  };
+  // online softmax of a block's scores: moves the running maximum (rescaling
+  // the accumulator and the denominator when it moves), adds the block's
+  // weights to the denominator and returns them as the two 16-bit parts
+  auto softmax = [&](int buf, const f32x4& s0, const f32x4& s1, T& phi, T& plo) {
     const uint32_t f0 = *reinterpret_cast<const uint32_t*>(&vflag[buf][4 * g]);
     const uint32_t f1 = *reinterpret_cast<const uint32_t*>(&vflag[buf][16 + 4 * g]);
     float sv[8];
@@ -385,13 +370,15 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     }
     den += ps;
     m = mn;
-    const T phi = __builtin_bit_cast(T, u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                              hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)});
-    const T plo = __builtin_bit_cast(T, u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                              lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)});
-    // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot 8 g + j], one 16-byte
-    // read; the lo product of tile d - 1 is issued between the hi products of
-    // tiles d and d + 1, so no MFMA waits on the one just before it
+    phi = __builtin_bit_cast(T, u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
+                                      hi[6] | (hi[7] << 16)});
+    plo = __builtin_bit_cast(T, u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+                                      lo[6] | (lo[7] << 16)});
+  };
+  // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot 8 g + j], one 16-byte read;
+  // the lo product of tile d - 1 is issued between the hi products of tiles d
+  // and d + 1, so no MFMA waits on the one just before it
+  auto weighted_sum = [&](int buf, const T& phi, const T& plo) {
     auto afrag = [&](int d) {
       const int dim = 16 * d + r;
       const int chunk = g ^ ((dim >> 3) & 3);
@@ -407,7 +394,51 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
       aprev = a;
     }
     acc[kANdt - 1] = M::run(aprev, plo, acc[kANdt - 1]);
-    if (b + 1 < nb) stage(buf ^ 1, rnext);   // fetched a block and a half ago
+  };
+
+  // Software pipeline over the blocks: iteration b runs block b + 1's scores
+  // and softmax beside block b's weighted sum, so the softmax arithmetic and
+  // the LDS latencies overlap the MFMAs.  Both LDS buffers hold staged blocks
+  // (b and b + 1); block b + 2 is staged into b's buffers once every
+  // wavefront is done with them.  Rows are gathered three blocks ahead into
+  // two register sets used in turn (block j's rows in set j mod 2; the loop
+  // is unrolled by two so that the sets are fixed registers), their indices
+  // one block ahead of the rows.
+  Rows ra, rb;
+  T phi = {}, plo = {};
+  if (nb > 0) {
+    load_idx(0);
+    fetch(0, ra);
+    stage(0, ra);
+    if (nb > 1) {
+      load_idx(1);
+      fetch(1, rb);
+      stage(1, rb);
+    }
+    if (nb > 2) {
+      load_idx(2);
+      fetch(2, ra);
+    }
+    if (nb > 3) load_idx(3);
+    __syncthreads();
+    f32x4 s0, s1;
+    scores(0, s0, s1);
+    softmax(0, s0, s1, phi, plo);
+  }
+  // rstage holds block b + 2's rows; rfetch (block b + 1's, staged) takes block b + 3's
+  auto block = [&](int b, const Rows& rstage, Rows& rfetch) {
+    const int buf = b & 1;
+    if (b + 3 < nb) fetch(b + 3, rfetch);
+    if (b + 4 < nb) load_idx(b + 4);
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    if (b + 1 < nb) scores(buf ^ 1, s0, s1);
+    weighted_sum(buf, phi, plo);
+    if (b + 1 < nb) softmax(buf ^ 1, s0, s1, phi, plo);
+    if (b + 2 < nb) {
+      __syncthreads();   // every wavefront is done with block b's buffers
+      stage(buf, rstage);
+      __syncthreads();   // block b + 2 is visible
+    }
   };
   for (int b = 0; b < nb; b += 2) {
     block(b, ra, rb);
