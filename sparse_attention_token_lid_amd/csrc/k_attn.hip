@@ -213,9 +213,8 @@ template <> struct AMfma<2> {
   static __device__ __forceinline__ f32x4 run(T a, T b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ uint32_t to16(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;   // round to nearest even
+  static __device__ __forceinline__ uint32_t to16(float x) {   // hardware conversion, ties to even
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
   }
   static __device__ __forceinline__ float from16(uint32_t b) { return __uint_as_float(b << 16); }
 };
