@@ -96,7 +96,7 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
       const int64_t row = v[i] ? ri : 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        r[i][c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kv + row * L + coff[c]));
+        r[i][c] = *reinterpret_cast<const u32x4*>(kv + row * L + coff[c]);   // cached: the query's other heads re-read it
     }
   };
   auto consume = [&](const u32x4 (&r)[G][NCH], const bool (&v)[G]) {
@@ -172,10 +172,9 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 // registers three blocks ahead (their indices four blocks ahead), and writes
 // both LDS copies (double-buffered) two blocks ahead.  The blocks are
 // software-pipelined: block b + 1's S^T and softmax run beside block b's
-// weighted sum.  The transposed rows
-// (80 B pitch) swizzle their four chunks by (dim / 8) mod 4 so that both the
-// writes (lanes 8 dims apart) and the reads (16 consecutive dims) spread
-// over the banks.
+// weighted sum.  The transposed rows (80 B pitch) swizzle their four chunks
+// by (dim / 8) mod 4 so that both the writes (lanes 8 dims apart) and the
+// reads (16 consecutive dims) spread over the banks.
 // The weights are split into two 16-bit parts, p = hi + lo (lo = the
 // rounding residual of hi), and both are multiplied in, so the weighted sum
 // keeps about 16 bits of each weight instead of the 8 of a single bf16; the
