@@ -76,9 +76,11 @@ def stored_traffic(workload: str, plan: str, splits: int):
     (profiles/traffic.json), or None if absent or measured on other kernels."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path)).get(workload)
+        data = json.load(open(path))
     except (OSError, ValueError):
         return None
+    # a workload's record under another entry point's kernel is keyed "<workload>:<plan>"
+    rec = data.get(f"{workload}:{plan}") or data.get(workload)
     if not rec or rec.get("kernel_hash") != kernel_source_hash(plan):
         return None
     if rec.get("plan") != plan or rec.get("splits") != splits:
