@@ -213,21 +213,23 @@ def test_attn_after_topk(lid):
     check(lid, qa, kv, idx, 1.0 / np.sqrt(L), "bf16", "after topk")
 
 
-def test_attn_full_size_sampled(lid):
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attn_full_size_sampled(lid, dtype):
     """The bench shape (512 queries x 16384 keys, 64 heads, L 512, 512
     selected per query), checked on a sample of queries that the oracle
     computes one by one."""
     n_tok, n_kv, H, L, k_sel = 512, 16384, 64, 512, 512
-    qa, kv = draw(n_tok, n_kv, H, L, "bf16", seed=13)
+    qa, kv = draw(n_tok, n_kv, H, L, dtype, seed=13)
     idx = li.draw_selection(n_tok, n_kv, k_sel, seed=13)
     scale = 1.0 / np.sqrt(L)
-    _say("attn full size: 512 x 16384, H 64, L 512, k_sel 512, bf16")
-    got = run(lid, qa, kv, idx, scale, "bf16")
+    _say(f"attn full size: 512 x 16384, H 64, L 512, k_sel 512, {dtype}")
+    got = run(lid, qa, kv, idx, scale, dtype)
     assert np.all(np.isfinite(got))
+    qk = "bf16" if dtype == "bf16" else None
     for t in (0, 1, 255, 511):
-        want = oracle.sparse_attn(qa[t:t + 1], kv, idx[t:t + 1], scale, qk_dtype="bf16")
+        want = oracle.sparse_attn(qa[t:t + 1], kv, idx[t:t + 1], scale, qk_dtype=qk)
         err = np.abs(got[t:t + 1].astype(np.float64) - want)
-        assert (err <= tolerance(qa[t:t + 1], kv, idx[t:t + 1], scale, "bf16")).all(), f"query {t}"
+        assert (err <= tolerance(qa[t:t + 1], kv, idx[t:t + 1], scale, dtype)).all(), f"query {t}"
 
 
 def test_attn_deterministic(lid):
