@@ -26,8 +26,11 @@
  *  - All arrays are C row-major and contiguous (mask rows have stride
  *    mask_ld).  q and k must be 16-byte aligned.
  *  - A key s is visible to query t iff lo_t <= s < hi_t and v[t,s] != -inf.
- *    Keys outside [lo_t, hi_t) are never scored and their mask entries are
- *    never read.  Masked keys (-inf) are never returned.
+ *    Keys outside [lo_t, hi_t) never enter query t's selection; their mask
+ *    entries have no effect, although the MFMA kernels may read them (only
+ *    inside [0, n_kv) of row t, where a workgroup's queries' ranges overlap)
+ *    so the whole [n_tok, n_kv] part of a mask must be readable.  Masked keys
+ *    (-inf) are never returned.
  *  - Rows with fewer than k_top visible keys are padded with idx = -1 and
  *    score = -inf after the visible keys.
  *  - A score of -0 is reported as +0 (and ties with +0 by index).
@@ -42,12 +45,16 @@
  *    LID_ERR_HIP (a launch failed; outputs undefined).  There is no fallback
  *    to a path that would need an n_tok x n_kv buffer.
  *  - Calls that share one workspace must not overlap in time.
- *  - The workspace must be zero-filled before its first use (the decode plan
- *    keeps one 32-bit completion counter per query at its start, the prefill
- *    plan with key splits one per block of 8 queries, 4 when k_top > 512);
- *    every call
- *    that completes leaves those counters at zero again, so a workspace is
- *    zeroed once and then reused freely, also from a captured HIP graph.
+ *  - Workspace layout: every non-empty workspace starts with a 4096-byte
+ *    counter region, and the plan's data follows it.  The plans that finish
+ *    inside their scoring kernel (decode; prefill with a few key splits) keep
+ *    32-bit completion counters there (one per query, or per block of 8
+ *    queries; at most 1024); no entry point writes anything else into it.
+ *    The region must be zero before the first call on a workspace; every call
+ *    that completes leaves it at zero again.  So a workspace is zero-filled
+ *    once and can then be reused for any later shape, plan or entry point
+ *    (lid_topk, lid_topk_fp8, lid_topk_shared), also from a captured HIP
+ *    graph.
  */
 #ifndef LID_H
 #define LID_H
@@ -108,7 +115,8 @@ size_t lid_topk_workspace_size(const lid_shape* shape);
  *   idx       [n_tok, k_top]    int32 output
  *   score     [n_tok, k_top]    f32 output (the v of each returned key), or NULL
  *   workspace device scratch of >= lid_topk_workspace_size(shape) bytes,
- *             8-byte aligned, zero-filled before its first use (see above)
+ *             8-byte aligned, its first 4096 bytes zero before its first use
+ *             (see above)
  *   stream    hipStream_t
  * Inputs must be finite (q, k, w); a NaN or +inf score is not detected. */
 int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* w,
@@ -174,9 +182,10 @@ int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, co
  *   idx       [k_top]  int32 output (-1 after the selectable keys)
  *   score     [k_top]  f32 output (-inf after them), or NULL
  *   workspace device scratch of >= lid_topk_shared_workspace_size(shape)
- *             bytes, 8-byte aligned (no zero-fill needed): the partial sums
- *             of U per key and query chunk (O(n_kv), not O(n_tok * n_kv)) and
- *             the per-chunk sorted lists
+ *             bytes, 8-byte aligned: after the 4096-byte counter region
+ *             (left untouched, so that a zeroed workspace can be shared with
+ *             lid_topk), the partial sums of U per key and query chunk
+ *             (O(n_kv), not O(n_tok * n_kv)) and the per-chunk sorted lists
  * k_top, plan and splits: k_top as for lid_topk; plan and splits are ignored.
  * Asynchronous on `stream`; errors as for lid_topk. */
 size_t lid_topk_shared_workspace_size(const lid_shape* shape);

@@ -200,8 +200,9 @@ def topk_shared(q, k, w, mask=None, kv_range=None, k_top=512, *, idx=None, score
             raise ValueError(f"{name} must be a contiguous tensor on {dev}")
     if k.dtype != q.dtype or k.shape[1] != D or w.shape != (n_tok, H) or w.dtype != torch.float32:
         raise ValueError("dtype/shape mismatch among q, k, w")
-    if mask is not None and (mask.dim() != 2 or mask.shape[0] != n_tok):
-        raise ValueError("mask must be float16 [n_tok, mask_ld]")
+    if mask is not None:
+        if mask.dtype not in (torch.float16, torch.int16, torch.uint16) or mask.dim() != 2 or mask.shape[0] != n_tok:
+            raise ValueError("mask must be float16 [n_tok, mask_ld]")
     if kv_range is not None and (kv_range.dtype != torch.int32 or tuple(kv_range.shape) != (n_tok, 2)):
         raise ValueError("kv_range must be int32 [n_tok, 2]")
     shape = shape_for(q, k, k_top, mask)

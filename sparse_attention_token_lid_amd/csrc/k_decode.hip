@@ -885,13 +885,8 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
 
 template <int DT, int FORM>
 hipError_t launch_one(const KArgs& a, int keys_per_wg, int ch, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<DT, FORM>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&decode_kernel<DT, FORM>), 160 * 1024);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)(a.n_tok * a.P));
   hipLaunchKernelGGL((decode_kernel<DT, FORM>), grid, dim3(BS), decode_lds_bytes(keys_per_wg, a.K, a.P, ch, FORM), st,
                      a, keys_per_wg, ch);

@@ -83,13 +83,8 @@ __global__ __launch_bounds__(NWG * 64) void generic_kernel(KArgs a) {
 size_t generic_lds_bytes(int cap) { return (size_t)NWG * cap * 8 + (size_t)NWG * 256 * 4; }
 
 hipError_t launch_generic(const KArgs& a, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&generic_kernel), 160 * 1024);
+  if (e != hipSuccess) return e;
   const int64_t items = a.n_tok * a.P;
   dim3 grid((unsigned)((items + NWG - 1) / NWG));
   hipLaunchKernelGGL(generic_kernel, grid, dim3(NWG * 64), generic_lds_bytes(a.cap), st, a);

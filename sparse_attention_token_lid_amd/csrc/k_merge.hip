@@ -15,13 +15,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KArgs a, int ch) {
 size_t merge_lds_bytes(int P, int K, int ch) { return finish_lds_need(P, K, ch); }
 
 hipError_t launch_merge(const KArgs& a, int ch, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&merge_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&merge_kernel), 160 * 1024);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)a.n_tok), dim3(kMergeThreads), merge_lds_bytes(a.P, a.K, ch), st, a,
                      ch);
   return hipGetLastError();

@@ -202,9 +202,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // Workgroups go to the 8 XCDs round-robin (block b to XCD b % 8).  The
   // (query block, split) pairs are numbered so that each XCD gets a
   // contiguous run of them: the P splits of a query block share one XCD and
-  // its L2, which then fetches their queries from HBM once, not P times.
-  uint32_t g = blockIdx.x;
-  if (P > 1) {
+  // its L2, which then fetches their queries from HBM once, not P times; and
+  // consecutive query blocks, which see nearly the same keys (causal) or the
+  // same sequence's key block (several sequences in one batch), share one, so
+  // an XCD's L2 streams only the keys its own queries see.
+  uint32_t g;
+  {
     const uint32_t T = gridDim.x, x = blockIdx.x % 8u, i = blockIdx.x / 8u;
     const uint32_t Q = T / 8u, Rm = T % 8u;
     g = x * Q + (x < Rm ? x : Rm) + i;
@@ -599,13 +602,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
 template <int NW, int DT, bool MK, bool SC = false>
 hipError_t launch_one(const KArgs& a, hipStream_t st) {
   const size_t lds = prefill_lds_bytes(NW, a.cap);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<NW, DT, MK, SC>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 2 * kTileBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(&prefill_kernel<NW, DT, MK, SC>),
+                               160 * 1024 - 2 * kTileBytes);
+  if (e != hipSuccess) return e;
   const int64_t nqb = (a.n_tok + NW - 1) / NW;
   dim3 grid((unsigned)(nqb * a.P));
   hipLaunchKernelGGL((prefill_kernel<NW, DT, MK, SC>), grid, dim3(NW * 64), lds, st, a);

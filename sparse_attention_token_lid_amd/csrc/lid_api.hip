@@ -4,6 +4,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "lid.h"
 #include "lid_device.h"
 #include "lid_kernels.h"
@@ -20,6 +24,13 @@ constexpr int64_t kCUs = 256;          // MI355X compute units
 constexpr int kDecodeMaxSplits = 256;  // bounds the decode workspace independently of n_kv
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kTreeCapHost = 512;     // k_top range of the decode merge tree: next_pow2(k_top) == 512
+// Every workspace starts with a counter region of this fixed size; the data
+// of every plan follows it.  The finishing counters of the split plans live
+// there (at most kMaxCounters of them), every call leaves them at zero, and no
+// entry point writes anything else into the region: so a workspace that was
+// zeroed once stays valid for any later shape, plan or entry point.
+constexpr size_t kCounterRegion = 4096;
+constexpr int64_t kMaxCounters = (int64_t)(kCounterRegion / 4);
 
 struct Plan {
   int kind;         // lid_plan (never AUTO)
@@ -34,11 +45,14 @@ struct Plan {
   int fuse;         // prefill, P > 1: the scoring kernel finishes from the split lists itself
                     // (1: merging sorted lists, 2: selecting from unsorted ones)
   int64_t raw_ld;   // decode, raw form: scores per query row
-  size_t ws;        // workspace bytes
-  size_t ws_data;   // decode: offset of lists / raw scores (after the counters)
+  size_t ws;        // workspace bytes (0, or kCounterRegion + the plan's data)
+  bool counters;    // the plan keeps finishing counters in the counter region
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+std::mutex g_attr_mu;
+std::set<std::pair<const void*, int>> g_attr_done;  // (kernel, device) with the LDS limit raised
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 hipEvent_t g_prof_before = nullptr;  // recorded around the scoring kernel when set
@@ -111,15 +125,16 @@ int make_plan(const lid_shape* s, Plan* pl) {
     if (prefill_lds_bytes(pl->nw, pl->cap) + 2 * (size_t)kPrefillTile * kMfmaDim * 2 > kMaxLds)
       return LID_ERR_UNSUPPORTED;
     if (P > 1) {
-      // workspace: per-query-block counters (zero between launches), then the
-      // split lists; with few splits the last workgroup of a query block
-      // merges them (the register merge needs next_pow2(K) in 256..1024 and an
-      // even K)
+      // workspace: the split lists after the counter region; with few splits
+      // the last workgroup of a query block merges them, counted by one
+      // counter per query block (the register merge needs next_pow2(K) in
+      // 256..1024 and an even K); otherwise the merge kernel does it
       const int n2 = next_pow2(K);
-      const bool fusable = P <= kFuseMaxSplits && n2 >= 256 && n2 <= 1024 && K % 2 == 0;
+      const bool fusable = P <= kFuseMaxSplits && n2 >= 256 && n2 <= 1024 && K % 2 == 0 &&
+                           cdiv(s->n_tok, pl->nw) <= kMaxCounters;
       pl->fuse = !fusable ? 0 : ((int64_t)P * K <= 64 * kFuseSelectRows ? 2 : 1);
-      pl->ws_data = (size_t)cdiv(cdiv(s->n_tok, pl->nw) * 4, 256) * 256;
-      pl->ws = pl->ws_data + (size_t)s->n_tok * P * K * sizeof(uint64_t);
+      pl->counters = pl->fuse != 0;
+      pl->ws = kCounterRegion + (size_t)s->n_tok * P * K * sizeof(uint64_t);
       if (!pl->fuse) {
         pl->ch = merge_chunk(P, K);
         if (merge_lds_bytes(P, K, pl->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
@@ -132,6 +147,7 @@ int make_plan(const lid_shape* s, Plan* pl) {
       P = (int)(want < 1 ? 1 : (want > kDecodeMaxSplits ? kDecodeMaxSplits : want));
     }
     pl->P = P;
+    if (s->n_tok > kMaxCounters) return LID_ERR_UNSUPPORTED;  // one finishing counter per query
     int64_t kp = cdiv(cdiv(s->n_kv, 32), P) * 32;
     if (kp < 32) kp = 32;
     if (kp > kDecodeMaxKeys) return LID_ERR_UNSUPPORTED;
@@ -149,22 +165,22 @@ int make_plan(const lid_shape* s, Plan* pl) {
     pl->form = tc == 8 ? 3 : (tc ? 2 : (span <= kRawMax ? 1 : 0));
     if (P > 1 && pl->form == 0) pl->ch = merge_chunk(P, K);
     if (decode_lds_bytes(pl->keys_per_wg, K, P, pl->ch, pl->form) > kMaxLds) return LID_ERR_UNSUPPORTED;
-    // workspace: per-query counters (zero between launches), then the raw
+    // workspace: one counter per query in the counter region, then the raw
     // scores, the per-split lists or the summaries
-    pl->ws_data = (size_t)cdiv(s->n_tok * 4, 256) * 256;
+    pl->counters = true;
     if (pl->form == 1) {
       pl->raw_ld = cdiv(span, 64) * 64;
-      pl->ws = pl->ws_data + (size_t)s->n_tok * pl->raw_ld * sizeof(uint32_t);
+      pl->ws = kCounterRegion + (size_t)s->n_tok * pl->raw_ld * sizeof(uint32_t);
     } else if (pl->form >= 2) {
-      pl->ws = pl->ws_data + (size_t)s->n_tok * P * tc * sizeof(uint64_t);
+      pl->ws = kCounterRegion + (size_t)s->n_tok * P * tc * sizeof(uint64_t);
     } else {
-      pl->ws = pl->ws_data + (P > 1 ? (size_t)s->n_tok * P * K * sizeof(uint64_t) : 0);
+      pl->ws = kCounterRegion + (P > 1 ? (size_t)s->n_tok * P * K * sizeof(uint64_t) : 0);
     }
   }
   if (pl->P > 1 && kind == LID_PLAN_GENERIC) {
     pl->ch = merge_chunk(pl->P, K);
     if (merge_lds_bytes(pl->P, K, pl->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
-    pl->ws = (size_t)s->n_tok * pl->P * K * sizeof(uint64_t);
+    pl->ws = kCounterRegion + (size_t)s->n_tok * pl->P * K * sizeof(uint64_t);
   }
   // grid sizes must fit a 32-bit grid
   const int64_t blocks = (kind == LID_PLAN_PREFILL) ? cdiv(s->n_tok, pl->nw) * pl->P
@@ -175,6 +191,19 @@ int make_plan(const lid_shape* s, Plan* pl) {
 }
 
 }  // namespace
+
+namespace lid {
+hipError_t set_lds_limit(const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_attr_mu);
+  if (g_attr_done.count({kernel, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) g_attr_done.insert({kernel, dev});
+  return e;
+}
+}  // namespace lid
 
 extern "C" {
 
@@ -224,10 +253,9 @@ int topk_impl(const lid_shape* shape, const void* q, const float* q_scale, const
   a.kv_range = kv_range;
   a.idx = idx;
   a.score = score;
-  a.lists = reinterpret_cast<uint64_t*>(workspace);
-  if (pl.kind == LID_PLAN_DECODE || (pl.kind == LID_PLAN_PREFILL && pl.P > 1)) {
-    a.counters = reinterpret_cast<uint32_t*>(workspace);
-    unsigned char* data = reinterpret_cast<unsigned char*>(workspace) + pl.ws_data;
+  if (pl.ws > 0) {
+    unsigned char* data = reinterpret_cast<unsigned char*>(workspace) + kCounterRegion;
+    a.counters = pl.counters ? reinterpret_cast<uint32_t*>(workspace) : nullptr;
     a.lists = reinterpret_cast<uint64_t*>(data);
     a.raw = reinterpret_cast<uint32_t*>(data);
     a.raw_ld = pl.raw_ld;
@@ -362,7 +390,10 @@ int make_shared_plan(const lid_shape* s, SharedPlan* sp) {
     if (shared_merge_lds_bytes(sp->P, s->k_top, sp->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
   }
   if (groups * sp->nqc > INT32_MAX) return LID_ERR_UNSUPPORTED;
-  sp->ws_lists = (size_t)cdiv((int64_t)sp->nqc * s->n_kv * 4, 256) * 256;
+  // after the counter region (not used here, but kept out of, so that one
+  // workspace can serve lid_topk and lid_topk_shared): the partial sums, then
+  // the lists
+  sp->ws_lists = kCounterRegion + (size_t)cdiv((int64_t)sp->nqc * s->n_kv * 4, 256) * 256;
   sp->ws = sp->ws_lists + (sp->P > 1 ? (size_t)sp->P * s->k_top * sizeof(uint64_t) : 0);
   return LID_OK;
 }
@@ -400,7 +431,7 @@ int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const 
   a.kv_range = kv_range;
   a.idx = idx;
   a.score = score;
-  a.scores = reinterpret_cast<float*>(workspace);
+  a.scores = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + kCounterRegion);
   a.scores_ld = s.n_kv;
   a.lists = reinterpret_cast<uint64_t*>(reinterpret_cast<unsigned char*>(workspace) + sp.ws_lists);
   a.n_tok = s.n_tok;

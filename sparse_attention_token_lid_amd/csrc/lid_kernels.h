@@ -47,6 +47,10 @@ constexpr int kSharedListKeys = 4096;  // shared top-k: keys per selection workg
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
 constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <= 64 x this keys
 
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (kernel, device); thread-safe.
+hipError_t set_lds_limit(const void* kernel, int bytes);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st);
 hipError_t launch_prefill_scores(const KArgs& a, hipStream_t st);  // score-only mode, 8 queries per workgroup

@@ -60,12 +60,12 @@ def test_auto_plans_and_workspace(L, name, plan):
     ws = L.workspace_size(s)
     wl = li.WORKLOADS[name]
     lists = wl.n_tok * splits * wl.k_top * 8 if splits > 1 else 0
+    region = 4096  # fixed counter region at the start of every non-empty workspace
     if plan == "decode":
-        # per-query counters (256-byte rounded), then the split summaries
-        # (8 or 16 keys per split, the first size with which the splits hold
-        # 4 k_top to 4096 keys, 256 < k_top <= 512), else every 32-bit score of
-        # the query (ranges up to 32768 keys), else the split lists
-        counters = -(-wl.n_tok * 4 // 256) * 256
+        # the counter region, then the split summaries (8 or 16 keys per
+        # split, the first size with which the splits hold 4 k_top to 4096
+        # keys, 256 < k_top <= 512), else every 32-bit score of the query
+        # (ranges up to 32768 keys), else the split lists
         span = -(-wl.n_kv // 32) * 32
         raw = wl.n_tok * (-(-span // 64) * 64) * 4
         tc = 0
@@ -73,20 +73,34 @@ def test_auto_plans_and_workspace(L, name, plan):
             if not tc and 256 < wl.k_top <= 512 and 4 * wl.k_top <= c * splits <= 4096:
                 tc = c
         summaries = wl.n_tok * splits * tc * 8
-        assert ws == counters + (summaries if tc else raw if span <= 32768 else lists)
+        assert ws == region + (summaries if tc else raw if span <= 32768 else lists)
         assert tc == 8  # both decode workloads (k_top 512, 256 splits of 8-key summaries)
     elif splits > 1:
-        # per-query-block counters (8 queries per block at k_top <= 512),
-        # then the split lists
-        nw = 8 if wl.k_top <= 512 else 4
-        counters = -(-(-(-wl.n_tok // nw)) * 4 // 256) * 256
-        assert ws == counters + lists
+        # the counter region (one counter per block of 8 queries), then the
+        # split lists
+        assert ws == region + lists
     else:
         assert ws == 0
     # O(n_tok * k_top * splits) with splits <= 256, whatever n_kv is
-    assert splits <= 256 and ws <= 256 * -(-wl.n_tok * 4 // 256) + wl.n_tok * wl.k_top * 8 * 256
+    assert splits <= 256 and ws <= region + wl.n_tok * wl.k_top * 8 * 256
     if wl.n_kv >= 131072:
-        assert ws <= wl.n_tok * wl.n_kv * 4 // 4 + 256   # well below even the f32 score matrix
+        assert ws <= wl.n_tok * wl.n_kv * 4 // 4 + region   # well below even the f32 score matrix
+
+
+def test_counter_region_is_shape_independent(L):
+    """Every plan that needs a workspace reserves the same leading 4096-byte
+    counter region, so data of one shape never lands where another shape keeps
+    its counters: a workspace zeroed once serves any sequence of shapes."""
+    shapes = [shape_of("c2"), shape_of("dec1m"), shape_of("c3"), shape_of("c3", n_tok=1024, splits=2),
+              shape_of("c3", n_tok=64, splits=40), shape_of("c1", splits=4),
+              shape_of("c3", n_tok=4, plan=3), shape_of("c3", k_top=1024)]
+    for s in shapes:
+        ws = L.workspace_size(s)
+        assert ws == 0 or ws > 4096, (s.n_tok, s.splits, ws)
+    # a decode plan with more queries than counters is refused, not laid out differently
+    assert L.workspace_size(shape_of("c2", n_tok=1025, plan=3)) == 0
+    with pytest.raises(L.LidError):
+        L.plan_of(shape_of("c2", n_tok=1025, plan=3))
 
 
 def call(L, shape, q=16, k=16, w=16, mask=None, rng=None, idx=16, score=None, ws=None, ws_bytes=0):

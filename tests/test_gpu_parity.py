@@ -388,3 +388,48 @@ def test_no_score_matrix_allocated(lid, name):
     assert free1 == free0
     _say(f"[memory] {name}: workspace {ws_bytes / 2**20:.1f} MiB vs f32 score matrix "
          f"{wl.n_tok * wl.n_kv * 4 / 2**20:.0f} MiB; free memory unchanged")
+
+
+def test_workspace_reused_across_shapes(lid):
+    """One workspace, zeroed once, serves a sequence of different shapes,
+    plans and entry points: decode (split summaries), prefill with 1024
+    queries in 2 key splits (128 completion counters), the shared top-k (its
+    partial sums fill the data region), prefill with 4 splits, and decode
+    again.  Every plan keeps its counters in the same leading region and its
+    data after it, so no call finds another shape's data where its counters
+    are.  Exact inputs: bit-exact against the oracle on every call, and the
+    counter region is zero at the end."""
+    shapes = {
+        "dec": exact_inputs(1, 32768, seed=41),
+        "pf1024": exact_inputs(1024, 4096, seed=42),
+        "pf64": exact_inputs(64, 6000, seed=43),
+    }
+    plans = [("dec", 0, 0), ("pf1024", 2, 2), ("dec", 0, 0), ("shared", 0, 0), ("pf64", 2, 4), ("dec", 0, 0),
+             ("pf1024", 2, 2)]
+    need = 0
+    for name, plan, splits in plans:
+        q, k, w = shapes["pf64" if name == "shared" else name]
+        s = lid.make_shape(q.shape[0], k.shape[0], 64, 128, 512, lid.LID_F16, 0, plan, splits)
+        need = max(need, lid.workspace_size(s))
+        if name == "shared":
+            import ctypes
+            need = max(need, int(lid.load().lid_topk_shared_workspace_size(ctypes.byref(s))))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for name, plan, splits in plans:
+        _say(f"[parity] workspace reuse: {name} plan={plan} splits={splits}")
+        if name == "shared":
+            q, k, w = shapes["pf64"]
+            gi, gs = lid.topk_shared(to_dev(q, "f16"), to_dev(k, "f16"), to_dev(w, "f32"), k_top=512, workspace=ws)
+            torch.cuda.synchronize()
+            import oracle
+            oi, osc = oracle.topk_shared(q, k, w, k_top=512)[:2]
+            assert np.array_equal(gi.cpu().numpy(), oi) and np.array_equal(gs.cpu().numpy(), osc)
+            continue
+        q, k, w = shapes[name]
+        idx, sc = lid.topk(to_dev(q, "f16"), to_dev(k, "f16"), to_dev(w, "f32"), k_top=512, plan=plan,
+                           splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        rows = list(range(q.shape[0])) if q.shape[0] <= 64 else list(range(0, q.shape[0], 37)) + [q.shape[0] - 1]
+        o_idx, o_sc, _, v = oracle_rows(q, k, w, None, None, 512, rows)
+        check_rows(idx.cpu().numpy()[rows], sc.cpu().numpy()[rows], o_idx, o_sc, v, 0.0, rows=rows, exact=True)
+    assert int(ws[:4096].count_nonzero()) == 0, "the counter region is not back at zero"
