@@ -123,6 +123,26 @@ int lid_topk(const lid_shape* shape, const void* q, const void* k, const float* 
              const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* lid_topk without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  It computes exactly what lid_topk
+ * computes (the same kernels; bitwise-identical results) and allocates
+ * nothing: its scratch is a static device array of 16 MiB (16777216 bytes),
+ * one per GPU the library runs on, held until the process ends.  Its address
+ * is looked up (hipGetSymbolAddress) on the first call on each device, with
+ * the caller's current device, which must be the device of `stream`.
+ *   arguments  as for lid_topk (all device pointers, caller-owned)
+ *   returns    LID_ERR_WORKSPACE, before any launch, for a shape whose
+ *              lid_topk_workspace_size exceeds 16 MiB (e.g. a prefill plan
+ *              with many key splits and queries); other errors as lid_topk
+ * Every call on one GPU uses that GPU's one array: each call clears the
+ * array's counter region itself (a small kernel on `stream` before the
+ * scoring kernel), but calls that overlap in time on one GPU (on different
+ * streams or host threads) race on the array and give undefined results. */
+int lid_topk_noalloc(const lid_shape* shape, const void* q, const void* k, const float* w,
+                     const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
+                     void* stream);
+
 /* Score-only mode: the output of the pages' fused indexer op itself, without
  * the top-k.  ggml-org llama.cpp issue 25468, comment "Pinned: master is
  * missing the fused ggml_lightning_indexer op", gives that op's inputs (q, k,

@@ -27,7 +27,7 @@ PLAN_AUTO, PLAN_GENERIC, PLAN_PREFILL, PLAN_DECODE = 0, 1, 2, 3
 PLAN_NAMES = {PLAN_GENERIC: "generic", PLAN_PREFILL: "prefill", PLAN_DECODE: "decode"}
 STATUS = {0: "LID_OK", -1: "LID_ERR_INVALID_ARG", -2: "LID_ERR_UNSUPPORTED", -3: "LID_ERR_WORKSPACE",
           -4: "LID_ERR_HIP"}
-EXPORTS = ("lid_topk", "lid_topk_fp8", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores",
+EXPORTS = ("lid_topk", "lid_topk_noalloc", "lid_topk_fp8", "lid_topk_workspace_size", "lid_topk_plan", "lid_scores",
            "lid_topk_shared", "lid_topk_shared_workspace_size", "lid_sparse_attn",
            "lid_status_string", "lid_last_hip_error", "lid_set_profile_events", "lid_version")
 
@@ -66,6 +66,8 @@ def load():
         vp = ctypes.c_void_p
         lib.lid_topk.restype = ctypes.c_int
         lib.lid_topk.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.lid_topk_noalloc.restype = ctypes.c_int
+        lib.lid_topk_noalloc.argtypes = [ctypes.POINTER(LidShape), vp, vp, vp, vp, vp, vp, vp, vp]
         lib.lid_topk_workspace_size.restype = ctypes.c_size_t
         lib.lid_topk_workspace_size.argtypes = [ctypes.POINTER(LidShape)]
         lib.lid_topk_fp8.restype = ctypes.c_int
@@ -180,6 +182,43 @@ def topk(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits
                              _ptr(score), _ptr(workspace), ws_have, stream)
     if rc != 0:
         raise LidError(rc)
+    return idx, score
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the static scratch of lid_topk_noalloc, per GPU
+
+
+def topk_noalloc(q, k, w, mask=None, kv_range=None, k_top=512, *, plan=PLAN_AUTO, splits=0, idx=None, score=None,
+                 want_score=True, stream=None):
+    """lid_topk_noalloc: the fused top-k with the library's static scratch
+    instead of a workspace (no device allocation by the library; idx / score
+    are allocated here unless given).  f16 / bf16 / f32 q and k."""
+    import torch
+    n_tok = q.shape[0]
+    dev = q.device
+    if q.dim() != 3 or k.dim() != 2 or w.dim() != 2 or dev.type != "cuda":
+        raise ValueError("q [n_tok,H,D], k [n_kv,D], w [n_tok,H] on the GPU expected")
+    for name, t in (("q", q), ("k", k), ("w", w), ("mask", mask), ("kv_range", kv_range)):
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if k.dtype != q.dtype or q.dtype == torch.float8_e4m3fn or w.dtype != torch.float32:
+        raise ValueError("q and k f16 / bf16 / f32 of one dtype, w float32")
+    if mask is not None:
+        if mask.dtype not in (torch.float16, torch.int16, torch.uint16) or mask.dim() != 2 or mask.shape[0] != n_tok:
+            raise ValueError("mask must be float16 [n_tok, mask_ld]")
+    if kv_range is not None and (kv_range.dtype != torch.int32 or tuple(kv_range.shape) != (n_tok, 2)):
+        raise ValueError("kv_range must be int32 [n_tok, 2]")
+    shape = shape_for(q, k, k_top, mask, plan, splits)
+    if idx is None:
+        idx = torch.empty((n_tok, k_top), dtype=torch.int32, device=dev)
+    if score is None and want_score:
+        score = torch.empty((n_tok, k_top), dtype=torch.float32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = load().lid_topk_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(w), _ptr(mask), _ptr(kv_range),
+                                 _ptr(idx), _ptr(score), stream)
+    if rc != 0:
+        raise LidError(rc, "lid_topk_noalloc")
     return idx, score
 
 

@@ -12,6 +12,15 @@
 #include "lid_device.h"
 #include "lid_kernels.h"
 
+// The static scratch of lid_topk_noalloc: a device array of fixed size, one
+// copy per GPU (each at its own address), held until the process ends.  Host
+// code never uses the array's name as an address (on the host it is a
+// stand-in, not device memory): the address comes from hipGetSymbolAddress,
+// looked up once per device with that device current, and is kept per device
+// (scratch_address below).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 using namespace lid;
@@ -225,9 +234,19 @@ int lid_topk_plan(const lid_shape* shape, int32_t* splits_out) {
 
 namespace {
 
+// zeroes n 32-bit words (the counter region of the static scratch: a kernel,
+// not hipMemsetAsync, so that a captured graph replays it reliably)
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// clear_counters: zero the workspace's counter region on the stream before
+// the scoring kernel (the static scratch keeps whatever the previous call on
+// the device left there)
 int topk_impl(const lid_shape* shape, const void* q, const float* q_scale, const void* k, const float* k_scale,
               const float* w, const uint16_t* mask, const int32_t* kv_range, int32_t* idx, float* score,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream, bool clear_counters = false) {
   Plan pl;
   int rc = make_plan(shape, &pl);
   if (rc != LID_OK) return rc;
@@ -273,6 +292,11 @@ int topk_impl(const lid_shape* shape, const void* q, const float* q_scale, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
   hipError_t e;
+  if (clear_counters && pl.counters) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3((unsigned)kMaxCounters), 0, st,
+                       reinterpret_cast<uint32_t*>(workspace), (int)kMaxCounters);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e);
+  }
   if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
   if (pl.kind == LID_PLAN_PREFILL) e = launch_prefill(a, pl.nw, st);
   else if (pl.kind == LID_PLAN_DECODE) e = launch_decode(a, pl.keys_per_wg, pl.ch, pl.form, st);
@@ -284,6 +308,27 @@ int topk_impl(const lid_shape* shape, const void* q, const float* q_scale, const
     if (e != hipSuccess) return hip_fail(e);
   }
   return LID_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; null until looked up
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -301,6 +346,21 @@ int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, co
                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!shape || shape->qk_dtype != LID_F8E4M3 || !q_scale || !k_scale) return LID_ERR_INVALID_ARG;
   return topk_impl(shape, q, q_scale, k, k_scale, w, mask, kv_range, idx, score, workspace, workspace_bytes, stream);
+}
+
+int lid_topk_noalloc(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
+                     const int32_t* kv_range, int32_t* idx, float* score, void* stream) {
+  Plan pl;
+  int rc = make_plan(shape, &pl);
+  if (rc != LID_OK) return rc;
+  if (pl.ws > kScratchBytes) return LID_ERR_WORKSPACE;  // needs more than the static scratch holds
+  void* ws = nullptr;
+  if (pl.ws > 0 && shape->n_tok > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return topk_impl(shape, q, nullptr, k, nullptr, w, mask, kv_range, idx, score, ws, ws ? kScratchBytes : 0, stream,
+                   true);
 }
 
 int lid_scores(const lid_shape* shape, const void* q, const void* k, const float* w, const uint16_t* mask,
