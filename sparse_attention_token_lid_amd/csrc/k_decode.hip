@@ -447,6 +447,175 @@ __device__ __forceinline__ void tops_insert(TopsState& st, uint64_t key, int lan
   st.nbuf += n;
 }
 
+// ------------------------------------------ summary finish: one bucket pass
+// The K best (next_pow2(K) == kTreeCap) of the summary candidates, R per
+// thread (candidate i is x[i / BS] of thread i % BS; 0 = empty), sorted
+// descending into best[0..kTreeCap) and padded with 0, by one bucket pass.
+// The bucket of a key is floor((v - vmin) * 2048 / (vmax - vmin)), clamped
+// to 2047, over the candidates' score range [vmin, vmax]: each step of that
+// (a subtraction of one value, a product with one positive factor, a
+// truncation) is monotone in v, so a larger key never lands in a lower
+// bucket and equal scores share one.  A block scan over the 2048 bucket
+// counts, in descending bucket order, gives each bucket its first output
+// position; the keys of every bucket that starts below K are scattered into
+// a segment of their own, and a key's place inside its bucket is its rank
+// among that segment's keys (full 64-bit comparison: equal scores go by
+// index).  Keys placed at K or later are dropped.  No radix passes and no
+// sort network: six barriers.  Returns false before writing anything outside
+// its scratch (block-uniform) when a bucket holds more than kBucketMax keys
+// (many equal or nearly equal scores); the caller then takes the general
+// selection.  Scratch: H, S [kBuckets] u32, seg [K + kBucketMax] u64, red
+// [5 NW] u32.
+constexpr int kBucketBits = 11;
+constexpr int kBuckets = 1 << kBucketBits;
+constexpr int kBucketMax = 64;
+static_assert(kBuckets == 4 * BS, "four buckets per thread in the scan");
+
+// Maximum over the wavefront.  Each partner value is taken once, by every
+// lane, before the comparison: a lane exchange evaluated inside a divergent
+// select would read 0 from the lanes the select masked off.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  uint32_t y;
+  y = xor_lane_u32<1>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<2>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<4>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<8>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<16>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<32>(x);
+  x = __builtin_elementwise_max(x, y);
+  return x;
+}
+
+template <int R>
+__device__ __forceinline__ bool bucket_topk(const uint64_t (&x)[R], int K, uint64_t* best, uint32_t* H, uint32_t* S,
+                                            uint64_t* seg, uint32_t* red, int32_t* idx_row, float* score_row) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  // 1. smallest and largest score word of the present keys, their count;
+  //    the bucket counts cleared
+  uint32_t omin = ~0u, omax = 0u, c = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t h = (uint32_t)(x[r] >> 32);
+    omin = (x[r] && h < omin) ? h : omin;
+    omax = (x[r] && h > omax) ? h : omax;
+    c += x[r] ? 1u : 0u;
+  }
+  omin = ~wave_max_u32(~omin);
+  omax = wave_max_u32(omax);
+  c = wave_sum_u32(c);
+  if (lane == 0) { red[wv] = omin; red[NW + wv] = omax; red[2 * NW + wv] = c; }
+  *reinterpret_cast<u32x4*>(H + 4 * tid) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  omin = ~0u;
+  omax = 0u;
+  uint32_t n = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    omin = red[w] < omin ? red[w] : omin;
+    omax = red[NW + w] > omax ? red[NW + w] : omax;
+    n += red[2 * NW + w];
+  }
+  // scores are finite (-inf keys are never candidates); a range that is 0,
+  // infinite, or so small that the factor overflows puts every key in bucket 0
+  const float vmin = unord_f32(omin);
+  const float range = unord_f32(omax) - vmin;
+  float scale = range > 0.f ? (float)kBuckets / range : 0.f;
+  scale = (scale < 3.0e38f && range < 3.0e38f) ? scale : 0.f;
+  auto digit = [&](uint64_t key) -> uint32_t {
+    const uint32_t b = (uint32_t)((unord_f32((uint32_t)(key >> 32)) - vmin) * scale);
+    return b < (uint32_t)(kBuckets - 1) ? b : (uint32_t)(kBuckets - 1);
+  };
+  // 2. bucket counts
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (x[r]) atomicAdd(&H[digit(x[r])], 1u);
+  __syncthreads();
+  // 3. thread tid owns buckets kBuckets - 1 - 4 tid - e (e < 4): descending digits
+  uint32_t hc[4], sum = 0u, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hc[e] = H[kBuckets - 1 - 4 * tid - e];
+    sum += hc[e];
+    mx = hc[e] > mx ? hc[e] : mx;
+  }
+  const uint32_t incl = wave_incl_scan_u32(sum);
+  mx = wave_max_u32(mx);
+  if (lane == kWave - 1) red[3 * NW + wv] = incl;
+  if (lane == 0) red[4 * NW + wv] = mx;
+  __syncthreads();
+  uint32_t base = 0u, maxc = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wv ? red[3 * NW + w] : 0u;
+    maxc = red[4 * NW + w] > maxc ? red[4 * NW + w] : maxc;
+  }
+  if (maxc > (uint32_t)kBucketMax) return false;
+  uint32_t o = base + incl - sum;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int b = kBuckets - 1 - 4 * tid - e;
+    S[b] = o;  // first position of the bucket
+    H[b] = o;  // its fill cursor
+    o += hc[e];
+  }
+  __syncthreads();
+  // 4. the keys of the buckets that start below K, each bucket into its
+  //    segment (slots < K + kBucketMax)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (x[r]) {
+      const uint32_t d = digit(x[r]);
+      if (S[d] < (uint32_t)K) seg[atomicAdd(&H[d], 1u)] = x[r];
+    }
+  }
+  __syncthreads();
+  // 5. a key's place is its bucket's start plus its rank inside the bucket;
+  //    the first 8 entries of a segment are read at once (a segment holds
+  //    at most a few keys on random data; entries past its end are ignored,
+  //    and every read stays inside seg's K + kBucketMax + 8 entries).  The
+  //    selected keys go to best and straight to the output row as well.
+  uint32_t st[R], en[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t d = digit(x[r]);
+    st[r] = S[d];
+    en[r] = H[d];
+    const bool sel = x[r] != 0ull && st[r] < (uint32_t)K;
+    st[r] = sel ? st[r] : 0u;
+    en[r] = sel ? en[r] : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    uint64_t sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = seg[st[r] + j];
+    uint32_t pos = st[r];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pos += (st[r] + j < en[r] && sv[j] > x[r]) ? 1u : 0u;
+    for (uint32_t j = st[r] + 8; j < en[r]; ++j) pos += seg[j] > x[r] ? 1u : 0u;
+    if (en[r] > st[r] && pos < (uint32_t)K) {
+      best[pos] = x[r];
+      idx_row[pos] = key_index(x[r]);
+      if (score_row) score_row[pos] = key_score(x[r]);
+    }
+  }
+  const int nsel = n < (uint32_t)K ? (int)n : K;
+  for (int i = nsel + tid; i < kTreeCap; i += BS) {
+    best[i] = 0ull;
+    if (i < K) {
+      idx_row[i] = -1;
+      if (score_row) score_row[i] = -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
 template <int DT, int FORM>
 __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg, int ch) {
   constexpr bool TOPS = FORM == kFormTops || FORM == kFormTops8;
@@ -821,17 +990,40 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     int* s_pick = reinterpret_cast<int*>(smem + L.ints + 16);
     const uint64_t* sums = a.lists + (size_t)t * P * kTopsC;
     const int m0 = P * kTopsC;  // <= 4096 (host-checked)
-    for (int i = tid; i < m0; i += BS) {
-      const uint64_t key = __hip_atomic_load(&sums[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      cand[i] = key;
-      if (i % kTopsC == kTopsC - 1) lastc[i / kTopsC] = key;
-    }
-    for (int i = tid; i < P; i += BS) done[i] = 0;
-    if (tid == 0) *s_emax = 0ull;
-    __syncthreads();
+    // the candidates, in registers (for the bucket pass) and in LDS
+    // First round: the bucket pass over the candidates in registers (the
+    // stage region past the candidates and the merge tree's buffer holds its
+    // two bucket arrays), unless a bucket is too full; then, and after a
+    // re-scored split, the radix select and sort or the merge tree.
+    uint32_t* bH = reinterpret_cast<uint32_t*>(smem + 6144 * 8);
+    uint32_t* bS = bH + kBuckets;
+    static_assert(6144 * 8 + 2 * kBuckets * 4 <= kStageBytes, "bucket arrays fit the stage region");
+    static_assert(kTreeCap + kBucketMax + 8 <= 2048, "the bucket segments fit the merge tree's buffer");
+    auto load_and_bucket = [&](auto rr) -> bool {
+      constexpr int R = decltype(rr)::value;
+      uint64_t xk[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = r * BS + tid;
+        xk[r] = i < m0 ? __hip_atomic_load(&sums[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        if (i < m0) {
+          cand[i] = xk[r];
+          if (i % kTopsC == kTopsC - 1) lastc[i / kTopsC] = xk[r];
+        }
+      }
+      for (int i = tid; i < P; i += BS) done[i] = 0;
+      if (tid == 0) *s_emax = 0ull;
+      __syncthreads();
+      return bucket_topk<R>(xk, K, best, bH, bS, alt, red, a.idx + t * K, a.score ? a.score + t * K : nullptr);
+    };
+    bool have_best = m0 <= 4 * BS ? load_and_bucket(std::integral_constant<int, 4>{})
+                                  : load_and_bucket(std::integral_constant<int, 4096 / BS>{});
+    bool row_written = have_best;  // the bucket pass wrote the output row as well
     int mc = m0;
     for (;;) {
-      if (mc > 2 * kTreeCap) {
+      if (have_best) {
+        have_best = false;
+      } else if (mc > 2 * kTreeCap) {
         // more than 1024 candidates: a register radix select cuts them to the K
         // best, which one key per thread then sorts (block bitonic sort, six
         // LDS stages for 512 keys); measured faster than the merge tree there
@@ -860,6 +1052,7 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
       __syncthreads();
       const int pe = *s_pick;
       if (tid == 0) { done[pe] = 1; *s_emax = 0ull; }
+      row_written = false;
       const int64_t eb0 = nblk * pe / P, eb1 = nblk * (pe + 1) / P;
       const int64_t slo = lo + eb0 * KB, shi = lo + eb1 * KB;  // the split's keys
       score_range(std::integral_constant<int, 1>{}, eb0, eb1, [&](int64_t b, int64_t s, float v) {
@@ -876,9 +1069,11 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
       const int ns = block_select_compact_any(ex, (int)((eb1 - eb0) * KB), K, cand + nb, nullptr, shs, red);
       mc = nb + ns;
     }
-    for (int i = tid; i < K; i += BS) {
-      a.idx[t * K + i] = key_index(best[i]);
-      if (a.score) a.score[t * K + i] = key_score(best[i]);
+    if (!row_written) {
+      for (int i = tid; i < K; i += BS) {
+        a.idx[t * K + i] = key_index(best[i]);
+        if (a.score) a.score[t * K + i] = key_score(best[i]);
+      }
     }
   }
 }

@@ -433,3 +433,22 @@ def test_workspace_reused_across_shapes(lid):
         o_idx, o_sc, _, v = oracle_rows(q, k, w, None, None, 512, rows)
         check_rows(idx.cpu().numpy()[rows], sc.cpu().numpy()[rows], o_idx, o_sc, v, 0.0, rows=rows, exact=True)
     assert int(ws[:4096].count_nonzero()) == 0, "the counter region is not back at zero"
+
+
+@pytest.mark.parametrize("n_kv,repeats", [(32768, 16), (131072, 64), (32768, 2), (1048576, 512)])
+def test_decode_bucket_pass_ties(lid, n_kv, repeats):
+    """The summary finish's bucket pass when equal scores share a bucket:
+    the score of key s is the j(s)-th f16 value above 1, with j a scrambled
+    index that every key shares with repeats - 1 others, so the top 512 cut through
+    groups of equal scores and equal scores must go by index.  With 16 or 2
+    repeats every bucket holds at most 64 keys and the bucket pass decides
+    alone (ties ranked inside a bucket); with 64 and 512 repeats the buckets
+    overflow and the general selection takes over.  Bit exact."""
+    q, k, w, rng = _one_head_inputs(1, n_kv, seed=repeats)
+    distinct = n_kv // repeats
+    j = (np.arange(n_kv, dtype=np.int64) * 7919) % distinct       # each value exactly `repeats` times
+    k16 = k.astype(np.float16)
+    # the j-th f16 value from 1.0 up (distinct < 2^14 keeps it finite): ascending in j
+    k16[:, 0] = (0x3C00 + j).astype(np.uint16).view(np.float16)
+    parity(lid, q.astype(np.float16), k16, w, None, None, 512, "f16", 3, 0, exact=True,
+           label=f"decode-bucket/ties{repeats}")
