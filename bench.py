@@ -118,8 +118,10 @@ def visible_pairs(wl, ranges):
     return int((ranges[:, 1].astype("int64") - ranges[:, 0]).clip(min=0).sum())
 
 
-def cpu_baseline(d, form, seconds, rows_hint=None):
-    """Time the CPU oracle on a bounded sample of the same workload."""
+def cpu_baseline(d, form, seconds, gpu_idx=None):
+    """Time the CPU oracle on a bounded sample of the same workload.  With
+    the GPU's output rows (gpu_idx, host array), also report how many of the
+    sampled rows have exactly the oracle's index set ("exact_match")."""
     import numpy as np
 
     import oracle
@@ -130,11 +132,21 @@ def cpu_baseline(d, form, seconds, rows_hint=None):
     mask = d["mask"] if form == "mask" else None
     rng_arg = ranges if form == "ranges" else None
 
+    last = {}
+
     def run(rows):
         t0 = time.perf_counter()
-        oracle.topk(d["q"], d["k"], d["w"], mask=mask, kv_range=rng_arg, k_top=wl.k_top, rows=rows,
-                    threads=threads)
+        o_idx = oracle.topk(d["q"], d["k"], d["w"], mask=mask, kv_range=rng_arg, k_top=wl.k_top, rows=rows,
+                            threads=threads)[0]
+        last["rows"], last["idx"] = list(rows), o_idx
         return time.perf_counter() - t0
+
+    def exact_match():
+        if gpu_idx is None:
+            return None
+        same = sum(set(gpu_idx[r][gpu_idx[r] >= 0].tolist()) == set(o[o >= 0].tolist())
+                   for r, o in zip(last["rows"], last["idx"]))
+        return {"rows": len(last["rows"]), "identical_index_sets": int(same)}
 
     def pairs_of(rows):
         if ranges is None:
@@ -149,7 +161,8 @@ def cpu_baseline(d, form, seconds, rows_hint=None):
             spent += run([0])
             reps += 1
         return {"value": pairs_of([0]) * reps / spent, "unit": "pairs/s", "cores": 1, "kind": "oracle",
-                "sample": f"the full workload (1 query x {wl.n_kv} keys) run {reps} times, {spent:.1f} s"}
+                "sample": f"the full workload (1 query x {wl.n_kv} keys) run {reps} times, {spent:.1f} s",
+                "exact_match": exact_match()}
     # many queries: spread a row sample over the host's cores, sized to the budget
     m = min(wl.n_tok, threads)
     rows = list(range(0, wl.n_tok, max(1, wl.n_tok // m)))[:m]
@@ -159,7 +172,8 @@ def cpu_baseline(d, form, seconds, rows_hint=None):
         rows = list(range(0, wl.n_tok, max(1, wl.n_tok // max(m2, 1))))[:max(m2, 1)]
         t = run(rows)
     return {"value": pairs_of(rows) / t, "unit": "pairs/s", "cores": min(threads, len(rows)), "kind": "oracle",
-            "sample": f"{len(rows)} of {wl.n_tok} queries (evenly spaced) with all their visible keys, {t:.1f} s"}
+            "sample": f"{len(rows)} of {wl.n_tok} queries (evenly spaced) with all their visible keys, {t:.1f} s",
+            "exact_match": exact_match()}
 
 
 # sparse-attention consumer: the prefill ubatch's shape (512 queries over
@@ -550,7 +564,9 @@ def run_topk(args, name, steps, warmup, cpu_seconds):
     }
     if cpu_seconds and not scores_mode and not fp8 and not shared_mode:
         log(f"[bench] timing the CPU oracle (~{cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(d, form, cpu_seconds)
+        # the last replay left the workload's result in idx: the oracle's
+        # sampled rows are compared with it
+        out["cpu_baseline"] = cpu_baseline(d, form, cpu_seconds, gpu_idx=idx.cpu().numpy())
     del sets, calls
     torch.cuda.empty_cache()
     return out

@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   auto room = [&]() {
     if (SC) return;
     st.count = __builtin_amdgcn_readfirstlane(st.count);  // keep it scalar (see uniform_u64)
-    if (st.count > st.cap - 2 * kWave) wave_topk_trim(st);
+    if (prefill_room(st.count, st.cap)) wave_topk_trim(st);
   };
   // Compactions are synchronised across the workgroup: a wave that could not
   // take a whole further tile (two units) raises its flag before the tile
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // slot after the next barrier, which every reader of it has passed.
   auto flag_need = [&](int it) {
     if (SC) return;
-    if (lane == 0) cflag[(it & 1) * NW + wv] = st.count > st.cap - 3 * kWave ? 1u : 0u;
+    if (lane == 0) cflag[(it & 1) * NW + wv] = prefill_flag(st.count, st.cap) ? 1u : 0u;
   };
   auto sync_compact = [&](int it) {
     if (SC) return;

@@ -101,7 +101,7 @@ int make_plan(const lid_shape* s, Plan* pl) {
   // FP8 has an MFMA path in the decode kernel only
   const bool mfma_ok = (s->qk_dtype == LID_F16 || s->qk_dtype == LID_BF16 || fp8) && mfma_shape;
   memset(pl, 0, sizeof(*pl));
-  pl->cap = 2 * K + 192;
+  pl->cap = prefill_cap(K);  // per-wave candidate slots (lid_budget.h)
   int kind = s->plan;
   if (kind == LID_PLAN_AUTO) {
     if (!mfma_ok) kind = LID_PLAN_GENERIC;

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lid_budget.h"
+
 namespace lid {
 
 constexpr int kWave = 64;
@@ -290,7 +292,6 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
 // whole bucket that holds the K-th key keeps at most kTrimSlack keys beyond K,
 // and the threshold becomes that bucket's floor (still <= the K-th key, so
 // nothing that can reach the final top-K is dropped).
-constexpr int kTrimSlack = 64;
 // Threshold of the K best among the nonzero keys x (R per lane, unique),
 // which must number more than K: the K-th largest key (EXACT), or the floor
 // of the 8-bit radix bucket that holds it once that bucket adds at most
@@ -384,7 +385,7 @@ __device__ __forceinline__ void wave_topk_reduce(WaveTopK& st) {
 // stream; the final one uses wave_topk_reduce.
 __device__ __forceinline__ void wave_topk_trim(WaveTopK& st) {
   if (st.cap <= kWave * kReduceRegRows) {
-    if (st.count > st.K + kTrimSlack) wave_topk_reduce_reg<kReduceRegRows, false>(st);
+    if (prefill_trim(st.count, st.K)) wave_topk_reduce_reg<kReduceRegRows, false>(st);
     return;
   }
   wave_topk_reduce(st);

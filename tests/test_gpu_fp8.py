@@ -71,11 +71,15 @@ def parity_fp8(lid, q8, qs, k8, ks, w, mask, ranges, k_top, rows=None, exact=Fal
     _say(f"[fp8]   ok: {n}/{len(rows)} rows with identical index sets, tol={tol:.3g}")
 
 
-@pytest.mark.parametrize("n_kv", [3000, 40000])
-def test_fp8_decode_exact(lid, n_kv):
-    """Decode kernel, raw-score (3000 keys) and split-list (40000 keys) finish:
-    small-integer E4M3 values, power-of-two scales and dyadic weights make
-    every score exact, so indices and scores must match bit for bit."""
+@pytest.mark.parametrize("n_kv,splits", [(3000, 0), (40000, 0), (40000, 100)])
+def test_fp8_decode_exact(lid, n_kv, splits):
+    """Decode kernel with each finish: raw scores (3000 keys: 24 splits whose
+    summaries could not hold 4 k_top, over a range short enough for the raw
+    form), split summaries of 8 keys (40000 keys in the library's 256
+    splits) and sorted split lists (40000 keys in 100 splits: too few for
+    the summaries, too long for the raw form).  Small-integer E4M3 values,
+    power-of-two scales and dyadic weights make every score exact, so indices
+    and scores must match bit for bit."""
     rng = np.random.default_rng(n_kv)
     n_tok = 4
     q8, k8 = small_int_fp8(rng, (n_tok, 64, 128)), small_int_fp8(rng, (n_kv, 128))
@@ -83,7 +87,8 @@ def test_fp8_decode_exact(lid, n_kv):
     ks = (2.0 ** rng.integers(-2, 3, n_kv)).astype(np.float32)
     w = rng.choice(np.array([0, 0.25, 0.5, 1, 2], np.float32), (n_tok, 64))
     ranges = np.array([[0, n_kv], [5, n_kv - 1], [n_kv // 3, n_kv // 3 + 700], [0, 0]], np.int32)
-    parity_fp8(lid, q8, qs, k8, ks, w, None, ranges, 512, exact=True, label=f"decode-exact/{n_kv}")
+    parity_fp8(lid, q8, qs, k8, ks, w, None, ranges, 512, exact=True, label=f"decode-exact/{n_kv}/s{splits}",
+               plan=3, splits=splits)
 
 
 @pytest.mark.parametrize("name", ["c2", "dec1m"])
