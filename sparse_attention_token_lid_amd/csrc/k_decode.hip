@@ -471,26 +471,6 @@ constexpr int kBuckets = 1 << kBucketBits;
 constexpr int kBucketMax = 64;
 static_assert(kBuckets == 4 * BS, "four buckets per thread in the scan");
 
-// Maximum over the wavefront.  Each partner value is taken once, by every
-// lane, before the comparison: a lane exchange evaluated inside a divergent
-// select would read 0 from the lanes the select masked off.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  uint32_t y;
-  y = xor_lane_u32<1>(x);
-  x = __builtin_elementwise_max(x, y);
-  y = xor_lane_u32<2>(x);
-  x = __builtin_elementwise_max(x, y);
-  y = xor_lane_u32<4>(x);
-  x = __builtin_elementwise_max(x, y);
-  y = xor_lane_u32<8>(x);
-  x = __builtin_elementwise_max(x, y);
-  y = xor_lane_u32<16>(x);
-  x = __builtin_elementwise_max(x, y);
-  y = xor_lane_u32<32>(x);
-  x = __builtin_elementwise_max(x, y);
-  return x;
-}
-
 template <int R>
 __device__ __forceinline__ bool bucket_topk(const uint64_t (&x)[R], int K, uint64_t* best, uint32_t* H, uint32_t* S,
                                             uint64_t* seg, uint32_t* red, int32_t* idx_row, float* score_row) {
@@ -556,14 +536,21 @@ __device__ __forceinline__ bool bucket_topk(const uint64_t (&x)[R], int K, uint6
   }
   if (maxc > (uint32_t)kBucketMax) return false;
   uint32_t o = base + incl - sum;
+  uint32_t used = 0u;  // end of the segments: the last bucket that starts below K ends there
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int b = kBuckets - 1 - 4 * tid - e;
     S[b] = o;  // first position of the bucket
     H[b] = o;  // its fill cursor
+    used = o < (uint32_t)K && o + hc[e] > used ? o + hc[e] : used;
     o += hc[e];
   }
+  used = wave_max_u32(used);
+  if (lane == 0) red[wv] = used;  // (slots 0 .. NW - 1 were last read before the previous barrier)
   __syncthreads();
+  used = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) used = red[w] > used ? red[w] : used;
   // 4. the keys of the buckets that start below K, each bucket into its
   //    segment (slots < K + kBucketMax)
 #pragma unroll
@@ -574,34 +561,27 @@ __device__ __forceinline__ bool bucket_topk(const uint64_t (&x)[R], int K, uint6
     }
   }
   __syncthreads();
-  // 5. a key's place is its bucket's start plus its rank inside the bucket;
-  //    the first 8 entries of a segment are read at once (a segment holds
-  //    at most a few keys on random data; entries past its end are ignored,
-  //    and every read stays inside seg's K + kBucketMax + 8 entries).  The
-  //    selected keys go to best and straight to the output row as well.
-  uint32_t st[R], en[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint32_t d = digit(x[r]);
-    st[r] = S[d];
-    en[r] = H[d];
-    const bool sel = x[r] != 0ull && st[r] < (uint32_t)K;
-    st[r] = sel ? st[r] : 0u;
-    en[r] = sel ? en[r] : 0u;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
+  // 5. a key's place is its bucket's start plus its rank inside the bucket.
+  //    The threads walk the filled segment slots [0, used) (the keys that
+  //    can be placed below K, about one per thread); the first 8 entries of a
+  //    key's segment are read at once (entries past its end are ignored, and
+  //    every read stays inside seg's K + kBucketMax + 8 entries).  The placed
+  //    keys go to best and straight to the output row as well.
+  for (uint32_t i = (uint32_t)tid; i < used; i += BS) {
+    const uint64_t key = seg[i];
+    const uint32_t d = digit(key);
+    const uint32_t st = S[d], en = H[d];
     uint64_t sv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = seg[st[r] + j];
-    uint32_t pos = st[r];
+    for (int j = 0; j < 8; ++j) sv[j] = seg[st + j];
+    uint32_t pos = st;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pos += (st[r] + j < en[r] && sv[j] > x[r]) ? 1u : 0u;
-    for (uint32_t j = st[r] + 8; j < en[r]; ++j) pos += seg[j] > x[r] ? 1u : 0u;
-    if (en[r] > st[r] && pos < (uint32_t)K) {
-      best[pos] = x[r];
-      idx_row[pos] = key_index(x[r]);
-      if (score_row) score_row[pos] = key_score(x[r]);
+    for (int j = 0; j < 8; ++j) pos += (st + j < en && sv[j] > key) ? 1u : 0u;
+    for (uint32_t j = st + 8; j < en; ++j) pos += seg[j] > key ? 1u : 0u;
+    if (pos < (uint32_t)K) {
+      best[pos] = key;
+      idx_row[pos] = key_index(key);
+      if (score_row) score_row[pos] = key_score(key);
     }
   }
   const int nsel = n < (uint32_t)K ? (int)n : K;

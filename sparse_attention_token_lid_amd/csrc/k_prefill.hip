@@ -174,6 +174,40 @@ __device__ __forceinline__ void wave_select_lists(const KArgs& a, int64_t t, Wav
   wave_write_row(st.buf, a.K, a.idx + t * a.K, a.score ? a.score + t * a.K : nullptr, nullptr);
 }
 
+// The k_top best of the P split lists of one query (P K <= 64 kFuseSelectRows
+// keys, 0 = empty), sorted, into the output row by one bucket pass
+// (wave_bucket_topk): all keys are read into registers at once (16-byte
+// agent-coherent loads, as above), the wave's candidate buffer holds the
+// pass's segments and `bins` its buckets.  Returns false (nothing written)
+// when a bucket overflows; the caller then selects by radix passes.
+__device__ __forceinline__ bool wave_bucket_lists(const KArgs& a, int64_t t, WaveTopK& st, uint32_t* bins,
+                                                  uint32_t* meta) {
+  constexpr int R = kFuseSelectRows;
+  const int lane = lane_id();
+  const int n = a.P * a.K, K = a.K;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint64_t*>(a.lists + (size_t)t * n), (short)0, n * 8, 0x00020000);
+  uint64_t x[R];
+#pragma unroll
+  for (int c = 0; c < R / 2; ++c) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (lane + kWave * c) * 16, 0, 16));
+    x[2 * c] = ((uint64_t)v[1] << 32) | v[0];
+    x[2 * c + 1] = ((uint64_t)v[3] << 32) | v[2];
+  }
+  int32_t* irow = a.idx + t * K;
+  float* srow = a.score ? a.score + t * K : nullptr;
+  const int m = wave_bucket_topk<R, 512>(x, K, bins, st.buf, meta, [&](int pos, uint64_t key) {
+    irow[pos] = key_index(key);
+    if (srow) srow[pos] = key_score(key);
+  });
+  if (m < 0) return false;
+  for (int i = m + lane; i < K; i += kWave) {
+    irow[i] = -1;
+    if (srow) srow[i] = -__builtin_inff();
+  }
+  return true;
+}
+
 // SC: score-only mode.  Every (query, key) score of the workgroup's chunk
 // is written to a.scores (f32, row stride a.scores_ld; -inf outside the
 // query's range or under a -inf mask) instead of entering a top-k: the output
@@ -555,7 +589,61 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
 
   if (SC) return;  // score-only mode: nothing to finish
 
-  if (has_q && a.fuse == 2) {
+  // The key tiles are free now (every wave has passed the last tile
+  // barrier): each wave takes 8 KiB of them for its bucket pass, 2 x 512
+  // bins and the segment bounds of up to 1024 keys.
+  constexpr int kBins = 512;
+  constexpr int kWaveLds = 8192;
+  static_assert(NW * kWaveLds <= 2 * kTileBytes, "bucket bins fit the key tiles");
+  unsigned char* wlds = reinterpret_cast<unsigned char*>(wv * kWaveLds < kTileBytes ? ktile0 : ktile1) +
+                        (wv * kWaveLds) % kTileBytes;
+  uint32_t* bins = reinterpret_cast<uint32_t*>(wlds);
+  uint32_t* meta = bins + 2 * kBins;
+  static_assert(2 * kBins * 4 + (512 + kWaveBucketMax) * 4 <= kWaveLds, "segment bounds fit");
+  const int K = a.K;
+  int32_t* irow = a.idx + t * K;
+  float* srow = a.score ? a.score + t * K : nullptr;
+  uint64_t* lrow = a.lists + ((size_t)t * P + p) * K;
+  // Where a sorted result is needed (the query's row with one split; sorted
+  // split lists for the merges), the K best come from one bucket pass over
+  // the buffer read into registers (it then serves as the pass's segments),
+  // instead of a radix cut and a sort network: into the output row, or as
+  // this split's list (agent-scope stores when the last workgroup of the
+  // query block reads it in this kernel).  A bucket that overflows sends the
+  // wave to the radix cut and sort below.  Unsorted split lists (a.fuse ==
+  // 2) keep the radix cut alone, which is cheaper than the pass there.
+  bool finished = false;
+  if (has_q && a.fuse != 2 && st.cap <= kWave * kReduceRegRows && K <= 512) {
+    uint64_t x[kReduceRegRows];
+#pragma unroll
+    for (int r = 0; r < kReduceRegRows; ++r) x[r] = lane + kWave * r < st.count ? st.buf[lane + kWave * r] : 0ull;
+    const int m = wave_bucket_topk<kReduceRegRows, kBins>(x, K, bins, st.buf, meta, [&](int pos, uint64_t key) {
+      if (P == 1) {
+        irow[pos] = key_index(key);
+        if (srow) srow[pos] = key_score(key);
+      } else if (a.fuse) {
+        __hip_atomic_store(lrow + pos, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        lrow[pos] = key;
+      }
+    });
+    if (m >= 0) {
+      for (int i = m + lane; i < K; i += kWave) {
+        if (P == 1) {
+          irow[i] = -1;
+          if (srow) srow[i] = -__builtin_inff();
+        } else if (a.fuse) {
+          __hip_atomic_store(lrow + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          lrow[i] = 0ull;
+        }
+      }
+      finished = true;
+    }
+  }
+
+  if (finished) {
+  } else if (has_q && a.fuse == 2) {
     // unsorted split list: the K best (all present keys if fewer), 0-padded
     wave_topk_reduce(st);
     uint64_t* out = a.lists + ((size_t)t * P + p) * a.K;
@@ -586,7 +674,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     __syncthreads();
     if (s_last && has_q) {
       const int n2 = next_pow2(a.K);
-      if (a.fuse == 2) {
+      if (a.fuse == 2 && a.K <= 512 && wave_bucket_lists(a, t, st, bins, meta)) {
+        // done by the bucket pass
+      } else if (a.fuse == 2) {
         if (n2 == 256) wave_select_lists<kFuseSelectRows, 4>(a, t, st);
         else if (n2 == 512) wave_select_lists<kFuseSelectRows, 8>(a, t, st);
         else wave_select_lists<kFuseSelectRows, 16>(a, t, st);

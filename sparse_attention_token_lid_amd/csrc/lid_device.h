@@ -567,6 +567,158 @@ __device__ inline void wave_write_row(const uint64_t* buf, int K, int32_t* idx_r
   }
 }
 
+// --------------------------------------------- wavefront bucket pass (top-K)
+// Maximum and minimum over the wavefront.  Every partner value is taken once,
+// by all lanes, before the comparison (a lane exchange evaluated inside a
+// divergent select would read 0 from the lanes the select masked off).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  uint32_t y;
+  y = xor_lane_u32<1>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<2>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<4>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<8>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<16>(x);
+  x = __builtin_elementwise_max(x, y);
+  y = xor_lane_u32<32>(x);
+  x = __builtin_elementwise_max(x, y);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) { return ~wave_max_u32(~x); }
+
+// The K best of one wavefront's nonzero keys x (R per lane, unique), in
+// descending order, by one bucket pass, without a radix select or a sort
+// network.  The bucket of a key is floor((v - vmin) * NB / (vmax - vmin)),
+// clamped to NB - 1, over the keys' score range: each step of that map (a
+// subtraction of one value, a product with one positive factor, a
+// truncation) is monotone in the score v, so a larger key never lands in a
+// lower bucket and equal scores share one.  The bucket counts, scanned in
+// descending order, give each bucket its first output position; the keys of
+// every bucket that starts below K are scattered into a segment of `seg`
+// (with the segment's bounds beside each key in `meta`), and a key's place
+// inside its bucket is its rank among that segment's keys (full 64-bit
+// comparison: equal scores go by index).  out(pos, key) is called once for
+// every pos < m = min(K, number of keys), by some lane of the wavefront.
+// Returns m, or -1 (wave-uniform; out never called) when a bucket that
+// starts below K holds more than kWaveBucketMax keys, for the caller's
+// general path.  LDS of this wavefront: bins 2 NB u32; seg K + kWaveBucketMax
+// + 8 u64 (it may be the buffer x was read from); meta K + kWaveBucketMax u32.
+constexpr int kWaveBucketMax = 64;
+
+template <int R, int NB, typename Out>
+__device__ __forceinline__ int wave_bucket_topk(const uint64_t (&x)[R], int K, uint32_t* bins, uint64_t* seg,
+                                                uint32_t* meta, Out&& out) {
+  static_assert(NB % (4 * kWave) == 0, "whole 16-byte bin groups per lane");
+  constexpr int PER = NB / kWave;  // bins per lane in the scan
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int lane = lane_id();
+  uint32_t* cnt = bins;       // counts, then fill cursors
+  uint32_t* start = bins + NB;
+  // 1. score range and count of the present keys; counts cleared
+  uint32_t omin = ~0u, omax = 0u, c = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t h = (uint32_t)(x[r] >> 32);
+    omin = (x[r] && h < omin) ? h : omin;
+    omax = (x[r] && h > omax) ? h : omax;
+    c += x[r] ? 1u : 0u;
+  }
+  omin = __builtin_amdgcn_readfirstlane(wave_min_u32(omin));
+  omax = __builtin_amdgcn_readfirstlane(wave_max_u32(omax));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(wave_sum_u32(c));
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) *reinterpret_cast<u32x4_t*>(cnt + 4 * (lane + kWave * i)) = u32x4_t{0u, 0u, 0u, 0u};
+  // finite scores only (-inf keys are never candidates); a range that is 0,
+  // infinite or so small that the factor overflows puts every key in bucket 0
+  const float vmin = unord_f32(omin);
+  const float range = unord_f32(omax) - vmin;
+  float scale = range > 0.f ? (float)NB / range : 0.f;
+  scale = (scale < 3.0e38f && range < 3.0e38f) ? scale : 0.f;
+  auto bucket = [&](uint64_t key) -> uint32_t {
+    const uint32_t b = (uint32_t)((unord_f32((uint32_t)(key >> 32)) - vmin) * scale);
+    return b < (uint32_t)(NB - 1) ? b : (uint32_t)(NB - 1);
+  };
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // 2. bucket counts
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (x[r]) atomicAdd(&cnt[bucket(x[r])], 1u);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // 3. lane L owns buckets NB - 1 - PER L - e (e < PER), in descending order
+  uint32_t hc[PER], sum = 0u;
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(cnt + NB - PER * (lane + 1) + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hc[PER - 1 - (4 * i + j)] = v[j];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) sum += hc[e];
+  uint32_t o = wave_incl_scan_u32(sum) - sum;
+  uint32_t used = 0u, mx = 0u;  // end of the last bucket that starts below K; the largest such bucket
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int b = NB - 1 - PER * lane - e;
+    start[b] = o;
+    cnt[b] = o;
+    const bool below = o < (uint32_t)K;
+    used = below && o + hc[e] > used ? o + hc[e] : used;
+    mx = below && hc[e] > mx ? hc[e] : mx;
+    o += hc[e];
+  }
+  if (__builtin_amdgcn_readfirstlane(wave_max_u32(mx)) > (uint32_t)kWaveBucketMax) return -1;
+  used = __builtin_amdgcn_readfirstlane(wave_max_u32(used));
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // 4. the keys of the buckets that start below K, each into its segment,
+  //    with the segment's bounds (a bucket ends where the next lower one
+  //    starts; the lowest ends at n)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (x[r]) {
+      const uint32_t d = bucket(x[r]);
+      const uint32_t st = start[d];
+      if (st < (uint32_t)K) {
+        const uint32_t en = d > 0 ? start[d - 1] : n;
+        const uint32_t slot = atomicAdd(&cnt[d], 1u);
+        seg[slot] = x[r];
+        meta[slot] = st | (en << 16);
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // 5. a key's place: its bucket's start plus its rank inside the bucket.
+  //    The lanes walk the filled slots [0, used), two at a time; the first 8
+  //    entries of a key's segment are read at once, entries past its end are
+  //    ignored.
+  auto place = [&](uint32_t i) {
+    const uint64_t key = seg[i];
+    const uint32_t mt = meta[i];
+    const uint32_t st = mt & 0xFFFFu, en = mt >> 16;
+    uint64_t sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = seg[st + j];
+    uint32_t pos = st;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pos += (st + j < en && sv[j] > key) ? 1u : 0u;
+    for (uint32_t j = st + 8; j < en; ++j) pos += seg[j] > key ? 1u : 0u;
+    if (pos < (uint32_t)K) out((int)pos, key);
+  };
+  for (uint32_t i = (uint32_t)lane; i < used; i += 2 * kWave) {
+    place(i);
+    if (i + kWave < used) place(i + kWave);
+  }
+  return n < (uint32_t)K ? (int)n : K;
+}
+
 // ------------------------------------------------------------ block-wide ops
 // All threads of the block call these (blockDim.x = BS, a multiple of 64,
 // 128 <= BS <= 1024).  Barriers are the expensive part, so each helper uses
