@@ -175,9 +175,11 @@ int lid_scores(const lid_shape* shape, const void* q, const void* k, const float
  *   q_scale  [n_tok, H] f32, > 0 and finite
  *   k_scale  [n_kv]     f32, > 0 and finite
  * Other arguments as for lid_topk (workspace: lid_topk_workspace_size of the
- * same shape).  H = 64, D = 128 with at most 4 queries runs on the decode
- * MFMA kernel (128 bytes per key instead of 256); other shapes on the
- * vector-ALU kernel; LID_PLAN_PREFILL is LID_ERR_UNSUPPORTED. */
+ * same shape).  H = 64, D = 128 runs on the MFMA kernels (128 bytes per key
+ * instead of 256): the decode kernel for at most 4 queries
+ * (v_mfma_f32_32x32x64_f8f6f4), the prefill kernel otherwise
+ * (v_mfma_f32_16x16x128_f8f6f4, the whole head dimension per instruction);
+ * other shapes run on the vector-ALU kernel. */
 int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, const void* k,
                  const float* k_scale, const float* w, const uint16_t* mask,
                  const int32_t* kv_range, int32_t* idx, float* score, void* workspace,

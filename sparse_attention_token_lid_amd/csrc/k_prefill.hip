@@ -54,12 +54,26 @@ template <> struct Mfma<2> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
 };
+// OCP FP8 E4M3 in both operands, K = 128 per instruction: the whole head
+// dimension in one MFMA (format codes 0, 0; no block scales).  Lane l holds
+// row l % 16 and the 32 bytes k = 32 (l / 16) ... + 31.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+template <> struct Mfma<3> {
+  typedef i32x8 T;
+  static __device__ __forceinline__ f32x4 run(T a, T b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+__device__ __forceinline__ i32x8 join8(u32x4 lo, u32x4 hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
 
 constexpr int H = kMfmaHeads;
 constexpr int D = kMfmaDim;
 constexpr int TN = kPrefillTile;              // keys per tile (8 blocks of 16)
-constexpr int kTileBytes = TN * D * 2;         // 32 KiB
-constexpr int kBlockBytes = 16 * D * 2;        // 4 KiB
+constexpr int kTileBytes = TN * D * 2;         // 32 KiB (one LDS tile buffer; FP8 tiles use half)
+// bytes per key row: 256 (f16 / bf16) or 128 (FP8)
+template <int DT> constexpr int row_bytes() { return DT == 3 ? D : 2 * D; }
 
 // One global_load_lds_dwordx4: lane l copies 16 bytes from gbase + voff into
 // LDS byte address lds_addr + 16 l (lds_addr wave-uniform).  M0, which
@@ -216,6 +230,12 @@ template <int NW, int DT, bool MK, bool SC>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   using M = Mfma<DT>;
   using T = typename M::T;
+  constexpr bool F8 = DT == 3;
+  static_assert(!(F8 && SC), "no FP8 score-only mode");
+  constexpr int RB = row_bytes<DT>();          // bytes per key row
+  constexpr int KS = F8 ? 1 : 4;               // MFMA k-steps per 16-key block
+  constexpr int kTB = TN * RB;                 // bytes per key tile
+  constexpr int kBlockBytes = 16 * RB;         // bytes per 16-key block
   // The two key-tile buffers are separate LDS objects, so the compiler can
   // tell that the asynchronous global->LDS copy into one buffer does not alias
   // reads of the other (otherwise it waits for the copy before every LDS read).
@@ -283,16 +303,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   const uint32_t wspan = whi > wlo ? (uint32_t)(whi - wlo) : 0u;  // empty if the chunk misses the range
 
   // this wave's query in MFMA A-operand layout (A[rb][j]: head 16 rb + lane % 16,
-  // dims 32 (lane / 16) + 8 j ... + 7) and the weights of the heads its
-  // accumulators hold (wr[rb][e]: head 16 rb + 4 (lane / 16) + e)
-  T A[4][4];
+  // dims 32 (lane / 16) + 8 j ... + 7; FP8: A[rb][0] holds dims 32 (lane / 16)
+  // ... + 31) and the weights of the heads its accumulators hold (wr[rb][e]:
+  // head 16 rb + 4 (lane / 16) + e; FP8: times the head's q scale, which is
+  // positive and so commutes with the ReLU)
+  T A[4][KS];
   float wr[4][4];
-  {
+  if constexpr (F8) {
+    const unsigned char* qrow = reinterpret_cast<const unsigned char*>(a.q) + (has_q ? t : 0) * H * D;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      u32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+      if (has_q) {
+        lo = *reinterpret_cast<const u32x4*>(qrow + (16 * rb + r16) * D + 32 * G);
+        hi = *reinterpret_cast<const u32x4*>(qrow + (16 * rb + r16) * D + 32 * G + 16);
+      }
+      A[rb][0] = join8(lo, hi);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = 16 * rb + 4 * G + e;
+        wr[rb][e] = has_q ? a.w[t * H + h] * a.q_scale[t * H + h] : 0.f;
+      }
+  } else {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (has_q ? t : 0) * H * D;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < KS; ++j) {
         u32x4 v = {0, 0, 0, 0};
         if (has_q) v = *reinterpret_cast<const u32x4*>(qrow + (16 * rb + r16) * D + 32 * G + 8 * j);
         A[rb][j] = __builtin_bit_cast(T, v);
@@ -323,18 +363,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // LDS reads and waits for all of them before every fragment use, so the
   // copy is kept out of its view and waited for explicitly (vmcnt(0) before
   // the barrier that ends a tile).
-  constexpr int kInstPerWave = kTileBytes / 1024 / NW;
-  static_assert(kInstPerWave * NW * 1024 == kTileBytes, "tile copy must divide evenly");
+  // (FP8 rows are 128 bytes: one instruction copies 8 rows, and the 16-byte
+  // chunk c of row r lives at chunk c ^ (r & 7).)
+  constexpr int LPR = RB / 16;                 // lanes (16-byte chunks) per row
+  constexpr int RPI = kWave / LPR;             // rows per 1 KiB instruction
+  constexpr int kInstPerWave = kTB / 1024 / NW;
+  static_assert(kInstPerWave * NW * 1024 == kTB, "tile copy must divide evenly");
   const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(a.k);
   const int n_kv = (int)a.n_kv;
   uint32_t goff[kInstPerWave];
 #pragma unroll
   for (int r = 0; r < kInstPerWave; ++r) {
-    const int row = 4 * (wv * kInstPerWave + r) + (lane >> 4);
-    goff[r] = (uint32_t)(row * (D * 2) + (((lane & 15) ^ (row & 15)) << 4));
+    const int row = RPI * (wv * kInstPerWave + r) + lane / LPR;
+    goff[r] = (uint32_t)(row * RB + (((lane % LPR) ^ (row % LPR)) << 4));
   }
   auto gload = [&](int tile, int buf) {
-    const unsigned char* tb = kbytes + (size_t)tile * kTileBytes;
+    const unsigned char* tb = kbytes + (size_t)tile * kTB;
     const uint32_t lds0 = (uint32_t)(uintptr_t)((buf ? ktile1 : ktile0) + wv * kInstPerWave * 512);
     if ((tile + 1) * TN <= n_kv) {
 #pragma unroll
@@ -343,8 +387,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       const int last = n_kv - 1 - tile * TN;  // last valid row of the tile
 #pragma unroll
       for (int r = 0; r < kInstPerWave; ++r) {
-        const int row = (int)(goff[r] >> 8);
-        const uint32_t off = row <= last ? goff[r] : goff[r] - (uint32_t)((row - last) * (D * 2));
+        const int row = (int)(goff[r] / RB);
+        const uint32_t off = row <= last ? goff[r] : goff[r] - (uint32_t)((row - last) * RB);
         dma_row4(tb, off, lds0 + 1024 * r);
       }
     }
@@ -359,16 +403,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     s = s < n_kv - 1 ? s : n_kv - 1;
     return __builtin_nontemporal_load(mrow + s);
   };
+  // FP8: this wave's k scales for 64 keys (lane l <-> key s0 + l), read one
+  // tile ahead like the mask
+  auto kload = [&](int s0) -> float {
+    if constexpr (!F8) return 1.f;
+    int s = s0 + lane;
+    s = s < n_kv - 1 ? s : n_kv - 1;
+    return wave_has_keys ? a.k_scale[s] : 1.f;
+  };
 
   // LDS byte offset of B fragment j (key row lane % 16 of a block, dims
-  // 32 (lane / 16) + 8 j ... + 7) inside a 16-key block
+  // 32 (lane / 16) + 8 j ... + 7) inside a 16-key block; FP8: the two 16-byte
+  // halves of the fragment (dims 32 (lane / 16) ... + 31)
   uint32_t foff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) foff[j] = (uint32_t)(r16 * (D * 2) + (((4 * G + j) ^ r16) << 4));
-  auto frags = [&](int buf, int blk, T (&bq)[4]) {
+  for (int j = 0; j < 4; ++j)
+    foff[j] = F8 ? (uint32_t)(r16 * RB + (((2 * G + (j & 1)) ^ (r16 & 7)) << 4))
+                 : (uint32_t)(r16 * RB + (((4 * G + j) ^ r16) << 4));
+  auto frag = [&](const unsigned char* kt, int j) -> T {
+    if constexpr (F8)
+      return join8(*reinterpret_cast<const u32x4*>(kt + foff[0]), *reinterpret_cast<const u32x4*>(kt + foff[1]));
+    else
+      return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + foff[j]));
+  };
+  auto frags = [&](int buf, int blk, T (&bq)[KS]) {
     const unsigned char* kt = reinterpret_cast<const unsigned char*>(buf ? ktile1 : ktile0) + blk * kBlockBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bq[j] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kt + foff[j]));
+    for (int j = 0; j < KS; ++j) bq[j] = frag(kt, j);
   };
 
   // Head reduction of one 16-key block, this lane's 16 heads, as one chain
@@ -400,6 +461,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     float p[4];
     int s0;
     uint16_t mb;
+    float ks;    // FP8: the key's scale (lane l <-> key s0 + l)
     bool live;
   };
   struct Slice {  // values carried between the slices of one hand-off
@@ -431,6 +493,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       }
     } else if (i == 5) {
       z.v = __uint_as_float(z.x0) + __uint_as_float(z.x1);
+      if (F8) z.v = z.v * u.ks;
       asm volatile("" : "+v"(z.v));
     } else if (i == 6) {
       if (MK) z.v = z.v + z.mf;
@@ -499,23 +562,45 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // pinned with scheduling barriers (the empty asm statements keep each group
   // of ops next to its MFMA; without them instruction selection moves the
   // whole epilogue behind the last MFMA).
-  auto step = [&](const T (&bq)[4], T (&nxt)[4], bool load_next, int nbuf, int nblk, f32x4 (&acc)[4],
+  auto step = [&](const T (&bq)[KS], T (&nxt)[KS], bool load_next, int nbuf, int nblk, f32x4 (&acc)[4],
                   const f32x4 (&prev)[4], const Unit* u) -> float {
     const unsigned char* kn = reinterpret_cast<const unsigned char*>(nbuf ? ktile1 : ktile0) + nblk * kBlockBytes;
     const f32x4 zero = {};
     float sum = 0.f;
     Slice z;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    if constexpr (F8) {
+      // four MFMAs (one per row block of 16 heads, the whole head dimension
+      // each), four terms of the head reduction and two hand-off slices after
+      // each; the next block's fragment is read behind the first
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const int i = 4 * j + rb;
-        acc[rb] = M::run(A[rb][j], bq[j], j == 0 ? zero : acc[rb]);
-        sum = __builtin_fmaf(wr[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
-        asm volatile("" : "+v"(sum));
-        if (load_next && j == 0) nxt[rb] = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(kn + foff[rb]));
-        if (u) insert_slice(*u, i, z);
+        acc[rb] = M::run(A[rb][0], bq[0], zero);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * rb + e;
+          sum = __builtin_fmaf(wr[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
+          asm volatile("" : "+v"(sum));
+        }
+        if (load_next && rb == 0) nxt[0] = frag(kn, 0);
+        if (u) {
+          insert_slice(*u, 2 * rb, z);
+          insert_slice(*u, 2 * rb + 1, z);
+        }
         __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int i = 4 * j + rb;
+          acc[rb] = M::run(A[rb][j], bq[j], j == 0 ? zero : acc[rb]);
+          sum = __builtin_fmaf(wr[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
+          asm volatile("" : "+v"(sum));
+          if (load_next && j == 0) nxt[rb] = frag(kn, rb);
+          if (u) insert_slice(*u, i, z);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     return sum;
@@ -523,9 +608,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
 
   const int ntile = c1 - c0;
   uint16_t mn0 = 0, mn1 = 0;  // mask bits of the next tile (keys 0-63, 64-127)
+  float kn0 = 1.f, kn1 = 1.f;  // FP8: k scales of the next tile
   if (ntile > 0) {
     mn0 = mload(c0 * TN);
     mn1 = mload(c0 * TN + 64);
+    kn0 = kload(c0 * TN);
+    kn1 = kload(c0 * TN + 64);
     gload(c0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -535,10 +623,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) { accA[rb][e] = 0.f; accB[rb][e] = 0.f; }
-  T bq0[4], bq1[4];
+  T bq0[KS], bq1[KS];
   Unit u0, u1;  // keys 0-63 and 64-127 of a tile
   u1.p[0] = u1.p[1] = u1.p[2] = 0.f;
   u1.mb = 0;
+  u1.ks = 1.f;
   // Pipeline over the eight 16-key blocks of each tile: step b issues the
   // MFMAs of block b and finishes the head reduction of block b - 1.  The 64
   // scores of blocks 0-3 are handed to the top-k during the step of block 5,
@@ -547,10 +636,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     const int tile = c0 + it;
     frags(buf, 0, bq0);
     const uint16_t mc0 = mn0, mc1 = mn1;
+    const float kc0 = kn0, kc1 = kn1;
     const bool more = it + 1 < ntile;
     if (more) {
       mn0 = mload((tile + 1) * TN);
       mn1 = mload((tile + 1) * TN + 64);
+      kn0 = kload((tile + 1) * TN);
+      kn1 = kload((tile + 1) * TN + 64);
       gload(tile + 1, buf ^ 1);
     }
     u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr);
@@ -562,11 +654,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr);
     u0.s0 = tile * TN;
     u0.mb = mc0;
+    u0.ks = kc0;
     u0.live = true;
     u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0);
     u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr);
     u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr);
     u1.mb = mc1;
+    u1.ks = kc1;
     flag_need(it);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed in LDS
     __syncthreads();
@@ -710,6 +804,10 @@ size_t prefill_lds_bytes(int nw, int cap) {
 
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {
   const bool mk = a.mask != nullptr;
+  if (a.dtype == 3) {
+    if (nw == 8) return mk ? launch_one<8, 3, true>(a, st) : launch_one<8, 3, false>(a, st);
+    return mk ? launch_one<4, 3, true>(a, st) : launch_one<4, 3, false>(a, st);
+  }
   if (a.dtype == 1) {
     if (nw == 8) return mk ? launch_one<8, 1, true>(a, st) : launch_one<8, 1, false>(a, st);
     return mk ? launch_one<4, 1, true>(a, st) : launch_one<4, 1, false>(a, st);

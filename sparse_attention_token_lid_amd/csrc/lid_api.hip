@@ -98,7 +98,6 @@ int make_plan(const lid_shape* s, Plan* pl) {
   const int K = s->k_top;
   const bool mfma_shape = s->n_head == kMfmaHeads && s->head_dim == kMfmaDim;
   const bool fp8 = s->qk_dtype == LID_F8E4M3;
-  // FP8 has an MFMA path in the decode kernel only
   const bool mfma_ok = (s->qk_dtype == LID_F16 || s->qk_dtype == LID_BF16 || fp8) && mfma_shape;
   memset(pl, 0, sizeof(*pl));
   pl->cap = prefill_cap(K);  // per-wave candidate slots (lid_budget.h)
@@ -106,10 +105,9 @@ int make_plan(const lid_shape* s, Plan* pl) {
   if (kind == LID_PLAN_AUTO) {
     if (!mfma_ok) kind = LID_PLAN_GENERIC;
     else if (s->n_tok <= kDecodeMaxTok && cdiv(s->n_kv, kDecodeMaxSplits) <= kDecodeMaxKeys) kind = LID_PLAN_DECODE;
-    else kind = fp8 ? LID_PLAN_GENERIC : LID_PLAN_PREFILL;
+    else kind = LID_PLAN_PREFILL;
   }
   if ((kind == LID_PLAN_PREFILL || kind == LID_PLAN_DECODE) && !mfma_ok) return LID_ERR_UNSUPPORTED;
-  if (kind == LID_PLAN_PREFILL && fp8) return LID_ERR_UNSUPPORTED;
   pl->kind = kind;
 
   if (kind == LID_PLAN_GENERIC) {

@@ -163,18 +163,22 @@ def test_scores_errors_before_launch(L):
 
 def test_fp8_entry_errors(L):
     """FP8 shapes: lid_topk refuses them (no scales), lid_topk_fp8 needs both
-    scales and takes no prefill plan, and lid_scores does not take FP8."""
+    scales, the MFMA plans take H 64 / D 128 (decode up to 4 queries, else
+    prefill; other shapes the vector-ALU kernel), and lid_scores does not
+    take FP8."""
     lib = L.load()
     s8 = shape_of("c2", qk_dtype=L.LID_F8E4M3)
     assert L.plan_of(s8)[0] == "decode"
-    assert L.plan_of(shape_of("c3", qk_dtype=L.LID_F8E4M3))[0] == "generic"
+    assert L.plan_of(shape_of("c3", qk_dtype=L.LID_F8E4M3))[0] == "prefill"
+    assert L.plan_of(shape_of("c4", qk_dtype=L.LID_F8E4M3))[0] == "prefill"
+    assert L.plan_of(shape_of("c1", qk_dtype=L.LID_F8E4M3))[0] == "generic"
     ws = L.workspace_size(s8)
     assert call(L, s8, ws=16, ws_bytes=ws) == -1                      # lid_topk: FP8 needs the scales
     f = lib.lid_topk_fp8
     assert f(ctypes.byref(s8), 16, None, 16, 16, 16, None, None, 16, None, 16, ws, None) == -1
     assert f(ctypes.byref(shape_of("c2")), 16, 16, 16, 16, 16, None, None, 16, None, 16, ws, None) == -1
     sp = shape_of("c3", qk_dtype=L.LID_F8E4M3, plan=L.PLAN_PREFILL)
-    assert f(ctypes.byref(sp), 16, 16, 16, 16, 16, None, None, 16, None, None, 0, None) == -2
+    assert f(ctypes.byref(sp), 16, 16, 16, 16, 16, None, None, 16, None, None, 0, None) == -3   # workspace
     assert lib.lid_scores(ctypes.byref(s8), 16, 16, 16, None, None, 16, s8.n_kv, None) == -2
 
 
