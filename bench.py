@@ -60,11 +60,11 @@ def log(msg):
 
 # the sources each plan's scoring kernel is compiled from
 PLAN_SOURCES = {
-    "decode": ["k_decode.hip", "lid_device.h", "lid_kernels.h", "lid_merge.h", "lid_select.h"],
-    "prefill": ["k_prefill.hip", "lid_device.h", "lid_kernels.h"],
-    "generic": ["k_generic.hip", "lid_device.h", "lid_kernels.h"],
-    "shared": ["k_shared.hip", "lid_device.h", "lid_kernels.h", "lid_select.h"],
-    "attn": ["k_attn.hip", "lid_device.h", "lid_kernels.h"],
+    "decode": ["k_decode.hip", "lid_device.h", "lid_budget.h", "lid_kernels.h", "lid_merge.h", "lid_select.h"],
+    "prefill": ["k_prefill.hip", "lid_device.h", "lid_budget.h", "lid_kernels.h"],
+    "generic": ["k_generic.hip", "lid_device.h", "lid_budget.h", "lid_kernels.h"],
+    "shared": ["k_shared.hip", "lid_device.h", "lid_budget.h", "lid_kernels.h", "lid_merge.h", "lid_select.h"],
+    "attn": ["k_attn.hip", "lid_device.h", "lid_budget.h", "lid_kernels.h"],
 }
 
 
