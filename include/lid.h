@@ -207,7 +207,8 @@ int lid_topk_fp8(const lid_shape* shape, const void* q, const float* q_scale, co
  *             bytes, 8-byte aligned: after the 4096-byte counter region
  *             (left untouched, so that a zeroed workspace can be shared with
  *             lid_topk), the partial sums of U per key and query chunk
- *             (O(n_kv), not O(n_tok * n_kv)) and the per-chunk sorted lists
+ *             (O(n_kv), not O(n_tok * n_kv)) and, above 16384 keys, the
+ *             sorted lists of the key chunks
  * k_top, plan and splits: k_top as for lid_topk; plan and splits are ignored.
  * Asynchronous on `stream`; errors as for lid_topk. */
 size_t lid_topk_shared_workspace_size(const lid_shape* shape);

@@ -75,30 +75,6 @@ constexpr int kTileBytes = TN * D * 2;         // 32 KiB (one LDS tile buffer; F
 // bytes per key row: 256 (f16 / bf16) or 128 (FP8)
 template <int DT> constexpr int row_bytes() { return DT == 3 ? D : 2 * D; }
 
-// One global_load_lds_dwordx4: lane l copies 16 bytes from gbase + voff into
-// LDS byte address lds_addr + 16 l (lds_addr wave-uniform).  M0, which
-// carries the LDS address, is saved and restored around it.  The caller waits
-// for completion with s_waitcnt vmcnt(0).
-__device__ __forceinline__ void dma_row4(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(gbase), "s"(lds_addr)
-      : "memory");
-}
-
-// out[lane] = bit lane of m ? a : b (one v_cndmask_b32 on a scalar lane mask)
-__device__ __forceinline__ float lane_select(uint64_t m, float a, float b) {
-  float r;
-  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
-  return r;
-}
-
 // The k_top best of the P sorted split lists of one query (row t of
 // a.lists: P lists of K keys, descending, 0 = empty), merged by one wavefront
 // in registers and written as the output row.  N = 64 E >= K entries per
@@ -563,7 +539,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // of ops next to its MFMA; without them instruction selection moves the
   // whole epilogue behind the last MFMA).
   auto step = [&](const T (&bq)[KS], T (&nxt)[KS], bool load_next, int nbuf, int nblk, f32x4 (&acc)[4],
-                  const f32x4 (&prev)[4], const Unit* u) -> float {
+                  const f32x4 (&prev)[4], const Unit* u, auto&& mid) -> float {
     const unsigned char* kn = reinterpret_cast<const unsigned char*>(nbuf ? ktile1 : ktile0) + nblk * kBlockBytes;
     const f32x4 zero = {};
     float sum = 0.f;
@@ -587,6 +563,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
           insert_slice(*u, 2 * rb + 1, z);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if (rb == 0) mid();
       }
     } else {
 #pragma unroll
@@ -600,6 +577,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
           if (load_next && j == 0) nxt[rb] = frag(kn, rb);
           if (u) insert_slice(*u, i, z);
           __builtin_amdgcn_sched_barrier(0);
+          if (i == 3) mid();
         }
       }
     }
@@ -624,6 +602,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { accA[rb][e] = 0.f; accB[rb][e] = 0.f; }
   T bq0[KS], bq1[KS];
+  if (ntile > 0) frags(0, 0, bq0);
+  const auto no_mid = [] {};
   Unit u0, u1;  // keys 0-63 and 64-127 of a tile
   u1.p[0] = u1.p[1] = u1.p[2] = 0.f;
   u1.mb = 0;
@@ -632,9 +612,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // MFMAs of block b and finishes the head reduction of block b - 1.  The 64
   // scores of blocks 0-3 are handed to the top-k during the step of block 5,
   // those of blocks 4-7 during the step of block 1 of the next tile.
+  // The tile barrier sits inside the step of block 7, after its first four
+  // MFMAs (block 7's fragments are in registers by then, so every wave is
+  // done reading this tile's buffer): right after it each wave reads block
+  // 0 of the next tile, and those reads complete behind block 7's remaining
+  // twelve MFMAs instead of stalling every wave at the start of the tile.
+  // bq0 holds block 0's fragments when a tile starts.
   auto tile_body = [&](int it, int buf) {
     const int tile = c0 + it;
-    frags(buf, 0, bq0);
     const uint16_t mc0 = mn0, mc1 = mn1;
     const float kc0 = kn0, kc1 = kn1;
     const bool more = it + 1 < ntile;
@@ -645,25 +630,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       kn1 = kload((tile + 1) * TN + 64);
       gload(tile + 1, buf ^ 1);
     }
-    u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr);
+    u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr, no_mid);
     u1.s0 = (tile - 1) * TN + 64;
     u1.live = it > 0;
-    u0.p[0] = step(bq1, bq0, true, buf, 2, accB, accA, &u1);
-    u0.p[1] = step(bq0, bq1, true, buf, 3, accA, accB, nullptr);
-    u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr);
-    u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr);
+    u0.p[0] = step(bq1, bq0, true, buf, 2, accB, accA, &u1, no_mid);
+    u0.p[1] = step(bq0, bq1, true, buf, 3, accA, accB, nullptr, no_mid);
+    u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr, no_mid);
+    u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr, no_mid);
     u0.s0 = tile * TN;
     u0.mb = mc0;
     u0.ks = kc0;
     u0.live = true;
-    u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0);
-    u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr);
-    u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr);
+    u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0, no_mid);
+    u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr, no_mid);
+    u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr, [&] {
+      flag_need(it);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed in LDS
+      __syncthreads();
+      if (more) frags(buf ^ 1, 0, bq0);
+    });
     u1.mb = mc1;
     u1.ks = kc1;
-    flag_need(it);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed in LDS
-    __syncthreads();
     sync_compact(it);
   };
   for (int it = 0; it < ntile; it += 2) {

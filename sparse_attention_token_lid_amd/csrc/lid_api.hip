@@ -422,6 +422,7 @@ struct SharedPlan {
   int qchunk;     // queries per chunk
   int P;          // selection workgroups (sorted lists) over the keys
   int ch;         // merge chunk when P > 1
+  bool one;       // one workgroup selects from every key (no lists, no merge)
   size_t ws;      // workspace bytes
   size_t ws_lists;  // offset of the lists
 };
@@ -439,10 +440,11 @@ int make_shared_plan(const lid_shape* s, SharedPlan* sp) {
   nqc = nqc < (s->n_tok > 0 ? s->n_tok : 1) ? nqc : (s->n_tok > 0 ? s->n_tok : 1);
   sp->nqc = (int)(nqc < 1 ? 1 : nqc);
   sp->qchunk = (int)(s->n_tok > 0 ? cdiv(s->n_tok, sp->nqc) : 1);
-  const int64_t P = cdiv(s->n_kv, kSharedListKeys);
+  sp->one = s->n_kv <= kSharedSelectKeys && shared_select_lds_bytes(s->k_top) <= kMaxLds;
+  const int64_t P = sp->one ? 1 : cdiv(s->n_kv, kSharedListKeys);
   if (P > kMaxSplits) return LID_ERR_UNSUPPORTED;
   sp->P = (int)(P < 1 ? 1 : P);
-  if (shared_lists_lds_bytes(s->k_top) > kMaxLds) return LID_ERR_UNSUPPORTED;
+  if (!sp->one && shared_lists_lds_bytes(s->k_top) > kMaxLds) return LID_ERR_UNSUPPORTED;
   if (sp->P > 1) {
     sp->ch = merge_chunk(sp->P, s->k_top);
     if (shared_merge_lds_bytes(sp->P, s->k_top, sp->ch) > kMaxLds) return LID_ERR_UNSUPPORTED;
@@ -505,7 +507,11 @@ int lid_topk_shared(const lid_shape* shape, const void* q, const void* k, const 
   if (g_prof_before && (e = hipEventRecord(g_prof_before, st)) != hipSuccess) return hip_fail(e);
   if ((e = launch_shared_scores(a, sp.qchunk, sp.nqc, st)) != hipSuccess) return hip_fail(e);
   if (g_prof_after && (e = hipEventRecord(g_prof_after, st)) != hipSuccess) return hip_fail(e);
-  if ((e = launch_shared_lists(a, sp.nqc, st)) != hipSuccess) return hip_fail(e);
+  if (sp.one) {
+    if ((e = launch_shared_select(a, sp.nqc, st)) != hipSuccess) return hip_fail(e);
+  } else if ((e = launch_shared_lists(a, sp.nqc, st)) != hipSuccess) {
+    return hip_fail(e);
+  }
   if (sp.P > 1) {
     if ((e = launch_shared_merge(a, sp.ch, st)) != hipSuccess) return hip_fail(e);
   }

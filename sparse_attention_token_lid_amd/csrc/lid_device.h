@@ -64,6 +64,30 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 }
 
 // ---------------------------------------------------------------- wave helpers
+// One global_load_lds_dwordx4: lane l copies 16 bytes from gbase + voff into
+// LDS byte address lds_addr + 16 l (lds_addr wave-uniform).  M0, which
+// carries the LDS address, is saved and restored around it.  The caller waits
+// for completion with s_waitcnt vmcnt(0).
+__device__ __forceinline__ void dma_row4(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
+
+// out[lane] = bit lane of m ? a : b (one v_cndmask_b32 on a scalar lane mask)
+__device__ __forceinline__ float lane_select(uint64_t m, float a, float b) {
+  float r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }

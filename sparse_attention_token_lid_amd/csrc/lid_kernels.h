@@ -42,7 +42,8 @@ constexpr int kDecodeMaxKeys = 8192;   // keys one decode workgroup scores (LDS 
 constexpr int kRawMax = 32768;         // decode, raw form: longest visible range per query
 constexpr int kDecodeTopsC = 16;       // decode, summary forms: keys in each split's summary (16, or 8)
 constexpr int kDecodeTopsMax = 4096;   // decode, summary forms: most summary keys per query (P C)
-constexpr int kSharedGroupKeys = 256;  // shared top-k: keys per scoring workgroup
+constexpr int kSharedGroupKeys = 512;  // shared top-k: keys per scoring workgroup (64 per wavefront)
+constexpr int kSharedSelectKeys = 16384;  // shared top-k: most keys for the one-workgroup selection
 constexpr int kSharedListKeys = 4096;  // shared top-k: keys per selection workgroup (one sorted list each)
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
 constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <= 64 x this keys
@@ -68,6 +69,8 @@ size_t decode_lds_bytes(int keys_per_wg, int K, int P, int ch, int form);
 hipError_t launch_shared_scores(const KArgs& a, int qchunk, int nqc, hipStream_t st);
 hipError_t launch_shared_lists(const KArgs& a, int nqc, hipStream_t st);
 size_t shared_lists_lds_bytes(int K);
+size_t shared_select_lds_bytes(int K);
+hipError_t launch_shared_select(const KArgs& a, int nqc, hipStream_t st);
 hipError_t launch_shared_merge(const KArgs& a, int ch, hipStream_t st);  // a.P lists of a.K -> the output row
 size_t shared_merge_lds_bytes(int P, int K, int ch);
 

@@ -281,4 +281,158 @@ __device__ __forceinline__ void block_topk_tree_any(uint64_t* buf, uint64_t* alt
   else block_topk_tree<8>(buf, alt, m, K, idx_row, score_row, out);
 }
 
+// ------------------------------------------------------------ one bucket pass
+// Block-wide top-K by one bucket pass (workgroups of kSelThreads threads).
+// The K best of the keys held in registers, R per thread (key i is
+// x[i / kSelThreads] of thread i % kSelThreads; 0 = empty), sorted
+// descending into the output row (idx_row / score_row, padded with -1 / -inf
+// up to K) and, if best is given, into best[0..npad) padded with 0.
+// The bucket of a key is floor((v - vmin) * 2048 / (vmax - vmin)), clamped
+// to 2047, over the candidates' score range [vmin, vmax]: each step of that
+// (a subtraction of one value, a product with one positive factor, a
+// truncation) is monotone in v, so a larger key never lands in a lower
+// bucket and equal scores share one.  A block scan over the 2048 bucket
+// counts, in descending bucket order, gives each bucket its first output
+// position; the keys of every bucket that starts below K are scattered into
+// a segment of their own, and a key's place inside its bucket is its rank
+// among that segment's keys (full 64-bit comparison: equal scores go by
+// index).  Keys placed at K or later are dropped.  No radix passes and no
+// sort network: six barriers.  Returns false before writing anything outside
+// its scratch (block-uniform) when a bucket holds more than kBlockBucketMax keys
+// (many equal or nearly equal scores); the caller then takes the general
+// selection.  Scratch: H, S [kBlockBuckets] u32, seg [K + kBlockBucketMax] u64, red
+// [5 kSelWaves] u32.
+constexpr int kBlockBucketBits = 11;
+constexpr int kBlockBuckets = 1 << kBlockBucketBits;
+constexpr int kBlockBucketMax = 64;
+static_assert(kBlockBuckets == 4 * kSelThreads, "four buckets per thread in the scan");
+
+template <int R>
+__device__ __forceinline__ bool block_bucket_topk(const uint64_t (&x)[R], int K, uint64_t* best, int npad, uint32_t* H,
+                                                  uint32_t* S, uint64_t* seg, uint32_t* red, int32_t* idx_row,
+                                                  float* score_row) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int BS = kSelThreads, NW = kSelWaves;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave;
+  // 1. smallest and largest score word of the present keys, their count;
+  //    the bucket counts cleared
+  uint32_t omin = ~0u, omax = 0u, c = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t h = (uint32_t)(x[r] >> 32);
+    omin = (x[r] && h < omin) ? h : omin;
+    omax = (x[r] && h > omax) ? h : omax;
+    c += x[r] ? 1u : 0u;
+  }
+  omin = ~wave_max_u32(~omin);
+  omax = wave_max_u32(omax);
+  c = wave_sum_u32(c);
+  if (lane == 0) { red[wv] = omin; red[NW + wv] = omax; red[2 * NW + wv] = c; }
+  *reinterpret_cast<u32x4*>(H + 4 * tid) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  omin = ~0u;
+  omax = 0u;
+  uint32_t n = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    omin = red[w] < omin ? red[w] : omin;
+    omax = red[NW + w] > omax ? red[NW + w] : omax;
+    n += red[2 * NW + w];
+  }
+  // scores are finite (-inf keys are never candidates); a range that is 0,
+  // infinite, or so small that the factor overflows puts every key in bucket 0
+  const float vmin = unord_f32(omin);
+  const float range = unord_f32(omax) - vmin;
+  float scale = range > 0.f ? (float)kBlockBuckets / range : 0.f;
+  scale = (scale < 3.0e38f && range < 3.0e38f) ? scale : 0.f;
+  auto digit = [&](uint64_t key) -> uint32_t {
+    const uint32_t b = (uint32_t)((unord_f32((uint32_t)(key >> 32)) - vmin) * scale);
+    return b < (uint32_t)(kBlockBuckets - 1) ? b : (uint32_t)(kBlockBuckets - 1);
+  };
+  // 2. bucket counts
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (x[r]) atomicAdd(&H[digit(x[r])], 1u);
+  __syncthreads();
+  // 3. thread tid owns buckets kBlockBuckets - 1 - 4 tid - e (e < 4): descending digits
+  uint32_t hc[4], sum = 0u, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hc[e] = H[kBlockBuckets - 1 - 4 * tid - e];
+    sum += hc[e];
+    mx = hc[e] > mx ? hc[e] : mx;
+  }
+  const uint32_t incl = wave_incl_scan_u32(sum);
+  mx = wave_max_u32(mx);
+  if (lane == kWave - 1) red[3 * NW + wv] = incl;
+  if (lane == 0) red[4 * NW + wv] = mx;
+  __syncthreads();
+  uint32_t base = 0u, maxc = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    base += w < wv ? red[3 * NW + w] : 0u;
+    maxc = red[4 * NW + w] > maxc ? red[4 * NW + w] : maxc;
+  }
+  if (maxc > (uint32_t)kBlockBucketMax) return false;
+  uint32_t o = base + incl - sum;
+  uint32_t used = 0u;  // end of the segments: the last bucket that starts below K ends there
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int b = kBlockBuckets - 1 - 4 * tid - e;
+    S[b] = o;  // first position of the bucket
+    H[b] = o;  // its fill cursor
+    used = o < (uint32_t)K && o + hc[e] > used ? o + hc[e] : used;
+    o += hc[e];
+  }
+  used = wave_max_u32(used);
+  if (lane == 0) red[wv] = used;  // (slots 0 .. NW - 1 were last read before the previous barrier)
+  __syncthreads();
+  used = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) used = red[w] > used ? red[w] : used;
+  // 4. the keys of the buckets that start below K, each bucket into its
+  //    segment (slots < K + kBlockBucketMax)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (x[r]) {
+      const uint32_t d = digit(x[r]);
+      if (S[d] < (uint32_t)K) seg[atomicAdd(&H[d], 1u)] = x[r];
+    }
+  }
+  __syncthreads();
+  // 5. a key's place is its bucket's start plus its rank inside the bucket.
+  //    The threads walk the filled segment slots [0, used) (the keys that
+  //    can be placed below K, about one per thread); the first 8 entries of a
+  //    key's segment are read at once (entries past its end are ignored, and
+  //    every read stays inside seg's K + kBlockBucketMax + 8 entries).  The placed
+  //    keys go to best and straight to the output row as well.
+  for (uint32_t i = (uint32_t)tid; i < used; i += BS) {
+    const uint64_t key = seg[i];
+    const uint32_t d = digit(key);
+    const uint32_t st = S[d], en = H[d];
+    uint64_t sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = seg[st + j];
+    uint32_t pos = st;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pos += (st + j < en && sv[j] > key) ? 1u : 0u;
+    for (uint32_t j = st + 8; j < en; ++j) pos += seg[j] > key ? 1u : 0u;
+    if (pos < (uint32_t)K) {
+      if (best) best[pos] = key;
+      idx_row[pos] = key_index(key);
+      if (score_row) score_row[pos] = key_score(key);
+    }
+  }
+  const int nsel = n < (uint32_t)K ? (int)n : K;
+  for (int i = nsel + tid; i < (best && npad > K ? npad : K); i += BS) {
+    if (best) best[i] = 0ull;
+    if (i < K) {
+      idx_row[i] = -1;
+      if (score_row) score_row[i] = -__builtin_inff();
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
 }  // namespace lid
