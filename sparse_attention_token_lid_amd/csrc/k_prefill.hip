@@ -220,9 +220,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* cand = reinterpret_cast<uint64_t*>(smem);
   uint32_t* hist = reinterpret_cast<uint32_t*>(cand + (size_t)NW * a.cap);
-  int64_t* rlo = reinterpret_cast<int64_t*>(hist + NW * 256);
-  int64_t* rhi = rlo + NW;
-  uint32_t* cflag = reinterpret_cast<uint32_t*>(rhi + NW);  // [2][NW] compaction requests
+  uint32_t* cflag = hist + NW * 256;  // [2][NW] compaction requests
   uint32_t& s_last = cflag[2 * NW];  // this workgroup is the last of its query block to finish
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -247,25 +245,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   const int64_t t = qb * NW + wv;
   const bool has_q = t < a.n_tok;
 
-  // visible range of this wave's query
-  int64_t lo = 0, hi = 0;
-  if (has_q) {
-    lo = 0;
-    hi = a.n_kv;
+  // visible range of query t2 (empty past n_tok)
+  auto qrange = [&](int64_t t2, int64_t& l, int64_t& h) {
+    l = 0;
+    h = 0;
+    if (t2 >= a.n_tok) return;
+    h = a.n_kv;
     if (a.kv_range) {
-      int64_t l0 = a.kv_range[2 * t], h0 = a.kv_range[2 * t + 1];
-      lo = l0 < 0 ? 0 : l0;
-      hi = h0 > a.n_kv ? a.n_kv : h0;
-      if (hi < lo) hi = lo;
+      const int64_t l0 = a.kv_range[2 * t2], h0 = a.kv_range[2 * t2 + 1];
+      l = l0 < 0 ? 0 : l0;
+      h = h0 > a.n_kv ? a.n_kv : h0;
+      if (h < l) h = l;
     }
-  }
-  if (lane == 0) { rlo[wv] = lo; rhi[wv] = hi; }
-  __syncthreads();
+  };
+  // this wave's range, and the union of the block's ranges, which every
+  // wave computes itself (wave-uniform loads; no LDS exchange and no
+  // barrier, so the first tile's copy is issued next to the q loads)
+  int64_t lo, hi;
+  qrange(t, lo, hi);
   int64_t ulo = INT64_MAX, uhi = 0;
   for (int w2 = 0; w2 < NW; ++w2) {
-    if (rhi[w2] > rlo[w2]) {
-      ulo = rlo[w2] < ulo ? rlo[w2] : ulo;
-      uhi = rhi[w2] > uhi ? rhi[w2] : uhi;
+    int64_t l2, h2;
+    qrange(qb * NW + w2, l2, h2);
+    if (h2 > l2) {
+      ulo = l2 < ulo ? l2 : ulo;
+      uhi = h2 > uhi ? h2 : uhi;
     }
   }
   if (ulo >= uhi) { ulo = 0; uhi = 0; }
@@ -786,7 +790,7 @@ hipError_t launch_one(const KArgs& a, hipStream_t st) {
 
 // dynamic part only; the two key tiles (2 x 32 KiB) are static LDS
 size_t prefill_lds_bytes(int nw, int cap) {
-  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 8 + 2 * (size_t)nw * 4 + 16;
+  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 4 + 16;
 }
 
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {
