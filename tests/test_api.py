@@ -241,3 +241,19 @@ def test_sparse_attn_argument_checks(L):
     assert call(n_tok=1 << 24, H=64, L=256) == -2
     assert call(n_tok=1 << 24, H=64, L=512) == -2
     assert call(n_tok=(1 << 24) - 1, H=64, L=512, qa=None) == -1   # fits: reaches the pointer checks
+
+
+def test_shared_selection_plan_boundary(L):
+    """lid_topk_shared: up to 16384 keys one workgroup selects from every key
+    and the workspace holds the partial sums alone; from 16385 keys it adds
+    the sorted lists of the 4096-key chunks.  The largest k_top (1024) still
+    fits the one-workgroup selection."""
+    lib = L.load()
+    ws = lambda **kw: lib.lid_topk_shared_workspace_size(ctypes.byref(shape_of("c3", **kw)))
+    # 16384 keys: 32 key groups of 512, 8 query chunks; 4 KiB counter region + 8 x 16384 f32
+    assert ws(n_kv=16384) == 4096 + 8 * 16384 * 4
+    assert ws(n_kv=16384, k_top=1024) == 4096 + 8 * 16384 * 4
+    # 16385 keys: 33 groups, still 8 chunks; the partial sums rounded to 256 B, then 5 lists of k_top keys
+    assert ws(n_kv=16385) == 4096 + ((8 * 16385 * 4 + 255) // 256) * 256 + 5 * 512 * 8
+    assert ws(n_kv=16385, k_top=1024) == 4096 + ((8 * 16385 * 4 + 255) // 256) * 256 + 5 * 1024 * 8
+    assert ws(n_kv=16384, k_top=1025) == 0                                 # beyond k_top's limit

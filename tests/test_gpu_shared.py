@@ -144,3 +144,25 @@ def test_shared_workload_c3(lid):
     f16 mask): the shared selection against the oracle."""
     d = li.make("c3")
     parity(lid, d["q"], d["k"], d["w"], d["mask"], None, 512, "f16", label="c3")
+
+
+@pytest.mark.parametrize("n_kv,k_top", [(16384, 512), (16384, 1024), (16385, 512), (16385, 1024)])
+def test_shared_selection_boundary(lid, n_kv, k_top):
+    """Either side of the one-workgroup selection's limit (16384 keys: every
+    register row full; 16385: the 4096-key lists and the merge), at k_top 512
+    and 1024, bit for bit on exactly representable sums (many equal U, so
+    the bucket pass and its fallback both get keys)."""
+    q, k, w, rng = exact_inputs(3, n_kv, seed=n_kv + k_top, dtype="f16")
+    mask = np.zeros((3, n_kv), np.float16)
+    mask[:, ::5] = np.float16(-0.25)
+    mask[1, 7000:7100] = -np.inf
+    parity(lid, q, k, w, mask, None, k_top, "f16", exact=True, label=f"boundary {n_kv}/{k_top}")
+
+
+def test_shared_all_equal_full_width(lid):
+    """16384 keys with q = 0: every U is +0, every bucket pass overflows, and
+    the radix-select fallback returns the first k_top keys in index order."""
+    q, k, w, _ = exact_inputs(4, 16384, seed=11, dtype="f16")
+    q[:] = 0
+    idx, sc = run_shared(lid, q, k, w, None, None, 1024, "f16")
+    assert idx.tolist() == list(range(1024)) and np.all(sc == 0)
