@@ -280,7 +280,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // this wave's visible keys inside the chunk (32-bit: n_kv < 2^31)
   const int wlo = (int)(lo > (int64_t)c0 * TN ? lo : (int64_t)c0 * TN);
   const int whi = (int)(hi < (int64_t)c1 * TN ? hi : (int64_t)c1 * TN);
-  const uint32_t wspan = whi > wlo ? (uint32_t)(whi - wlo) : 0u;  // empty if the chunk misses the range
 
   // this wave's query in MFMA A-operand layout (A[rb][j]: head 16 rb + lane % 16,
   // dims 32 (lane / 16) + 8 j ... + 7; FP8: A[rb][0] holds dims 32 (lane / 16)
@@ -300,13 +299,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       }
       A[rb][0] = join8(lo, hi);
     }
+    // the weights and q scales of row t (row 0 without a query: every load
+    // is issued before any is used, then zeroed)
+    const int64_t tw = has_q ? t : 0;
+    float wv[4][4], qv[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int h = 16 * rb + 4 * G + e;
-        wr[rb][e] = has_q ? a.w[t * H + h] * a.q_scale[t * H + h] : 0.f;
+        wv[rb][e] = a.w[tw * H + h];
+        qv[rb][e] = a.q_scale[tw * H + h];
       }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wr[rb][e] = has_q ? wv[rb][e] * qv[rb][e] : 0.f;
   } else {
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (has_q ? t : 0) * H * D;
 #pragma unroll
@@ -374,22 +382,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     }
   };
   // this wave's mask values for 64 keys (lane l <-> key s0 + l), read one
-  // tile ahead so that no wait on global memory sits in front of the MFMAs
+  // tile ahead so that no wait on global memory sits in front of the MFMAs.
+  // Every wave issues the load, so that exactly kAfterCopy loads follow each
+  // copy: a wave without a query or keys reads row 0, and its values are
+  // never used (its range test sets every key to -inf).  The loaded value is
+  // returned untouched: any use of it here would make the compiler wait for
+  // the load at once.
   const bool wave_has_keys = has_q && whi > wlo;
-  const uint16_t* mrow = (MK && wave_has_keys) ? a.mask + t * a.mask_ld : nullptr;
+  const uint16_t* mrow = MK ? a.mask + (wave_has_keys ? t * a.mask_ld : 0) : nullptr;
   auto mload = [&](int s0) -> uint16_t {
-    if (!mrow) return 0;
+    if constexpr (!MK) return 0;
     int s = s0 + lane;
     s = s < n_kv - 1 ? s : n_kv - 1;
     return __builtin_nontemporal_load(mrow + s);
   };
   // FP8: this wave's k scales for 64 keys (lane l <-> key s0 + l), read one
-  // tile ahead like the mask
+  // tile ahead like the mask (by every wave, likewise)
   auto kload = [&](int s0) -> float {
     if constexpr (!F8) return 1.f;
     int s = s0 + lane;
     s = s < n_kv - 1 ? s : n_kv - 1;
-    return wave_has_keys ? a.k_scale[s] : 1.f;
+    return a.k_scale[s];
   };
 
   // LDS byte offset of B fragment j (key row lane % 16 of a block, dims
@@ -589,13 +602,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   };
 
   const int ntile = c1 - c0;
-  uint16_t mn0 = 0, mn1 = 0;  // mask bits of the next tile (keys 0-63, 64-127)
-  float kn0 = 1.f, kn1 = 1.f;  // FP8: k scales of the next tile
+  // vector memory loads issued after a tile's copy (mask entries, k scales)
+  // and the s_waitcnt that waits for everything but them (vmcnt = that count;
+  // expcnt and lgkmcnt at their maxima: no wait)
+  constexpr int kAfterCopy = (MK ? 2 : 0) + (F8 ? 2 : 0);
+  constexpr int kWaitCopy = (kAfterCopy & 0xF) | ((kAfterCopy >> 4) << 14) | (7 << 4) | (15 << 8);
+  // mask bits (keys 0-63, 64-127) and FP8 k scales of a tile, one register
+  // set per tile parity: a tile's set is loaded at the previous tile's start
+  // and read where its hand-offs need it (step 6, and after step 7), so the
+  // loads have almost two tiles to arrive; the next tile's loads go to the
+  // other set, whose values were copied into the hand-offs by then
+  uint16_t mset[2][2] = {{0, 0}, {0, 0}};
+  float kset[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
   if (ntile > 0) {
-    mn0 = mload(c0 * TN);
-    mn1 = mload(c0 * TN + 64);
-    kn0 = kload(c0 * TN);
-    kn1 = kload(c0 * TN + 64);
+    mset[0][0] = mload(c0 * TN);
+    mset[0][1] = mload(c0 * TN + 64);
+    kset[0][0] = kload(c0 * TN);
+    kset[0][1] = kload(c0 * TN + 64);
     gload(c0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -624,15 +647,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // bq0 holds block 0's fragments when a tile starts.
   auto tile_body = [&](int it, int buf) {
     const int tile = c0 + it;
-    const uint16_t mc0 = mn0, mc1 = mn1;
-    const float kc0 = kn0, kc1 = kn1;
     const bool more = it + 1 < ntile;
     if (more) {
-      mn0 = mload((tile + 1) * TN);
-      mn1 = mload((tile + 1) * TN + 64);
-      kn0 = kload((tile + 1) * TN);
-      kn1 = kload((tile + 1) * TN + 64);
+      // the copy first: the tile barrier then waits for it alone, while the
+      // mask entries and k scales of the next tile (from HBM, used only a
+      // tile later) may still be in flight (kAfterCopy loads)
       gload(tile + 1, buf ^ 1);
+      mset[buf ^ 1][0] = mload((tile + 1) * TN);
+      mset[buf ^ 1][1] = mload((tile + 1) * TN + 64);
+      kset[buf ^ 1][0] = kload((tile + 1) * TN);
+      kset[buf ^ 1][1] = kload((tile + 1) * TN + 64);
     }
     u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr, no_mid);
     u1.s0 = (tile - 1) * TN + 64;
@@ -642,19 +666,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr, no_mid);
     u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr, no_mid);
     u0.s0 = tile * TN;
-    u0.mb = mc0;
-    u0.ks = kc0;
+    u0.mb = mset[buf][0];
+    u0.ks = kset[buf][0];
     u0.live = true;
     u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0, no_mid);
     u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr, no_mid);
     u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr, [&] {
       flag_need(it);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed in LDS
+      // this wave's part of the next tile has landed in LDS: every vector
+      // memory operation but the kAfterCopy issued after the copy is done
+      // (they complete in order; the compiler's own waits before the mask
+      // and scale values are used do not count the copy, so they can only
+      // wait longer, never too little)
+      __builtin_amdgcn_s_waitcnt(kWaitCopy);
       __syncthreads();
       if (more) frags(buf ^ 1, 0, bq0);
     });
-    u1.mb = mc1;
-    u1.ks = kc1;
+    u1.mb = mset[buf][1];
+    u1.ks = kset[buf][1];
     sync_compact(it);
   };
   for (int it = 0; it < ntile; it += 2) {
