@@ -836,11 +836,19 @@ __global__ __launch_bounds__(BS, 1) void decode_kernel(KArgs a, int keys_per_wg,
     static_assert(kTreeCap + kBlockBucketMax + 8 <= 2048, "the bucket segments fit the merge tree's buffer");
     auto load_and_bucket = [&](auto rr) -> bool {
       constexpr int R = decltype(rr)::value;
+      // every load is issued before any value is used (clamped index; the
+      // entries past m0 are replaced by 0 afterwards), so the R round trips
+      // overlap instead of following one another
       uint64_t xk[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int i = r * BS + tid;
-        xk[r] = i < m0 ? __hip_atomic_load(&sums[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        xk[r] = __hip_atomic_load(&sums[i < m0 ? i : 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = r * BS + tid;
+        xk[r] = i < m0 ? xk[r] : 0ull;
         if (i < m0) {
           cand[i] = xk[r];
           if (i % kTopsC == kTopsC - 1) lastc[i / kTopsC] = xk[r];
