@@ -139,7 +139,7 @@ int make_plan(const lid_shape* s, Plan* pl) {
       const int n2 = next_pow2(K);
       const bool fusable = P <= kFuseMaxSplits && n2 >= 256 && n2 <= 1024 && K % 2 == 0 &&
                            cdiv(s->n_tok, pl->nw) <= kMaxCounters;
-      pl->fuse = !fusable ? 0 : ((int64_t)P * K <= 64 * kFuseSelectRows ? 2 : 1);
+      pl->fuse = !fusable ? 0 : (P > kFuseMergeSplits && (int64_t)P * K <= 64 * kFuseSelectRows ? 2 : 1);
       pl->counters = pl->fuse != 0;
       pl->ws = kCounterRegion + (size_t)s->n_tok * P * K * sizeof(uint64_t);
       if (!pl->fuse) {

@@ -47,6 +47,9 @@ constexpr int kSharedSelectKeys = 16384;  // shared top-k: most keys for the one
 constexpr int kSharedListKeys = 4096;  // shared top-k: keys per selection workgroup (one sorted list each)
 constexpr int kFuseMaxSplits = 16;     // prefill: most splits merged inside the scoring kernel
 constexpr int kFuseSelectRows = 32;    // prefill: the finish selects from P K <= 64 x this keys
+constexpr int kFuseMergeSplits = 4;   // prefill: up to this many splits, sorted lists are merged
+                                      // (their bucket passes plus the register merges cost less
+                                      // than radix cuts plus one selection over P K keys)
 
 // Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
 // per (kernel, device); thread-safe.

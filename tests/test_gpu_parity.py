@@ -99,12 +99,14 @@ def test_exact_arithmetic_bit_exact(lid, plan, splits, dtype):
     parity(lid, q, k, w, None, ranges, 512, dtype, plan, splits, exact=True, label=f"exact/{dtype}")
 
 
-@pytest.mark.parametrize("splits,k_top", [(3, 200), (5, 300), (20, 512), (3, 1000), (4, 100), (16, 512), (3, 301)])
+@pytest.mark.parametrize("splits,k_top", [(3, 200), (4, 512), (5, 300), (6, 256), (20, 512), (3, 1000), (4, 100),
+                                          (16, 512), (3, 301)])
 def test_prefill_split_finish_forms(lid, splits, k_top):
     """Prefill with key splits: up to 16 splits with an even k_top whose
-    next_pow2 is in 256..1024 are merged inside the scoring kernel by the last
-    workgroup of a query block; more splits, or other k_top, go through the
-    merge kernel.
+    next_pow2 is in 256..1024 are finished inside the scoring kernel by the
+    last workgroup of a query block (up to 4 splits, or more than 2048 keys
+    in all lists: sorted lists merged; otherwise unsorted lists selected
+    from); more splits, or other k_top, go through the merge kernel.
     Exact inputs (ties included) must match the oracle bit for bit."""
     n_tok, n_kv = 13, 6100
     q, k, w = exact_inputs(n_tok, n_kv, seed=splits * 7 + k_top, dtype="f16")
