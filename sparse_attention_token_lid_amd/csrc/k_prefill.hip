@@ -331,6 +331,111 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       for (int e = 0; e < 4; ++e) wr[rb][e] = has_q ? a.w[t * H + 16 * rb + 4 * G + e] : 0.f;
   }
 
+  // |S| form of the head reduction (f16 and FP8 keys).  max(S, 0) is
+  // (S + |S|) / 2, so sum_h w_h max(S_h, 0) = sum_h (w_h / 2) |S_h| + qt . k
+  // with qt = (1/2) sum_h w_h q_h (FP8: w_h times the head's q scale and q_h
+  // the E4M3 values; the k scale multiplies both terms).  |S_h| is a free
+  // source modifier of the FMA, so the per-head work is one FMA instead of a
+  // v_med3 and an FMA.  The linear term of the workgroup's NW queries is one
+  // more 16-row MFMA block (f16, 16x16x32) per 16 keys for the whole
+  // workgroup: row 2 i + p holds part p of qt_i 2^e_i split into f16 high and
+  // low parts (22 bits of it; e_i puts its largest entry in [2^14, 2^15)),
+  // built in LDS (als: 16 rows of 128 dims, 16-byte chunk c of row r at
+  // chunk c ^ r) and held in registers (read again after a compaction, which
+  // is the kernel's register peak and so runs without them).  Wavefront b % NW computes the term for block b of
+  // every tile and hands it to the others through LDS: lin[tile parity]
+  // [query][key of the tile].  bf16 keys keep the v_med3 form (their parts
+  // would need three bf16 rows).
+  constexpr bool AB = DT != 2;
+  float* lin = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(cflag) + 2 * NW * 4 + 16);
+  unsigned char* als = reinterpret_cast<unsigned char*>(lin + 2 * NW * TN);
+  int* les = reinterpret_cast<int*>(als + 16 * D * 2);  // e of each query
+  f16x8 AL[4];   // the A operand in registers (row r16, dims 32 G + 8 j ... + 7)
+  // this lane's row of the linear term's A operand, dims 32 G + 8 j ... + 7
+  auto al_frag = [&](int j) -> f16x8 {
+    return *reinterpret_cast<const f16x8*>(als + r16 * 2 * D + ((4 * G + j) ^ r16) * 16);
+  };
+  float lsc[2];  // 2^-e of queries 2 G and 2 G + 1, the rows lane group G holds in the lin result
+  if constexpr (AB) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wr[rb][e] *= 0.5f;
+    // qt of this wave's query: each lane sums its heads 16 rb + r16 (the A
+    // layout) over dims 32 G ... + 31, then the 16 lanes of its group add up
+    // (xor butterfly: every lane of the group ends with the same sums)
+    const int64_t tw = has_q ? t : 0;
+    float wa[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      float wt = a.w[tw * H + 16 * rb + r16];
+      if constexpr (F8) wt *= a.q_scale[tw * H + 16 * rb + r16];
+      wa[rb] = has_q ? wt : 0.f;
+    }
+    float qt[32];
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) qt[c] = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if constexpr (F8) {
+        // E4M3 -> f32 in hardware (exact), two bytes per conversion
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(A[rb][0][e], false);
+          const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(A[rb][0][e], true);
+          qt[4 * e] = __builtin_fmaf(wa[rb], lo2[0], qt[4 * e]);
+          qt[4 * e + 1] = __builtin_fmaf(wa[rb], lo2[1], qt[4 * e + 1]);
+          qt[4 * e + 2] = __builtin_fmaf(wa[rb], hi2[0], qt[4 * e + 2]);
+          qt[4 * e + 3] = __builtin_fmaf(wa[rb], hi2[1], qt[4 * e + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) qt[c] = __builtin_fmaf(wa[rb], (float)A[rb][c >> 3][c & 7], qt[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      float x = qt[c];
+      x += __uint_as_float(xor_lane_u32<1>(__float_as_uint(x)));
+      x += __uint_as_float(xor_lane_u32<2>(__float_as_uint(x)));
+      x += __uint_as_float(xor_lane_u32<4>(__float_as_uint(x)));
+      x += __uint_as_float(xor_lane_u32<8>(__float_as_uint(x)));
+      qt[c] = 0.5f * x;
+      mx = __builtin_fmaxf(mx, __builtin_fabsf(qt[c]));
+    }
+    mx = __builtin_fmaxf(mx, __uint_as_float(xor_lane_u32<16>(__float_as_uint(mx))));
+    mx = __builtin_fmaxf(mx, __uint_as_float(xor_lane_u32<32>(__float_as_uint(mx))));
+    int e = 0;
+    if (mx > 0.f) {
+      e = 15 - __builtin_amdgcn_frexp_expf(mx);
+      e = e < -120 ? -120 : (e > 120 ? 120 : e);
+    }
+    // rows 2 wv (high parts, lane r16 = 0 of each group) and 2 wv + 1 (low
+    // parts, r16 = 1) of als, dims 32 G ... + 31 (chunks 4 G ... + 3); with
+    // NW < 8, wave 0 also clears the rows of the missing queries
+    if (r16 < 2) {
+      const int row = 2 * wv + r16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = __builtin_ldexpf(qt[8 * j + i], e);
+          const _Float16 h = (_Float16)x;
+          v[i] = r16 == 0 ? h : (_Float16)(x - (float)h);
+        }
+        *reinterpret_cast<f16x8*>(als + row * 2 * D + ((4 * G + j) ^ row) * 16) = v;
+      }
+    }
+    if (NW < 8 && wv == 0 && r16 >= 2 * NW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x4*>(als + r16 * 2 * D + ((4 * G + j) ^ r16) * 16) = u32x4{0, 0, 0, 0};
+    }
+    if (lane == 0) les[wv] = e;
+  }
+
   // Streaming top-k state.  Scores enter on an f32 test alone (v >= tau_v,
   // where tau_v is the score of the k_top-th best key at the last
   // compaction): every key that beats tau passes it, and the few that tie
@@ -425,6 +530,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     for (int j = 0; j < KS; ++j) bq[j] = frag(kt, j);
   };
 
+  // the per-head term: |S| (weights halved, linear term added per key) or max(S, 0)
+  auto hterm = [](float x) -> float {
+    if constexpr (AB) return __builtin_fabsf(x);
+    else return relu(x);
+  };
+
   // Head reduction of one 16-key block, this lane's 16 heads, as one chain
   // of fused multiply-adds in element order i = 4 rb + e (16 cycles apart in
   // step(), so the chain never waits).  step() below uses the same order, so
@@ -434,7 +545,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   auto epilogue = [&](const f32x4 (&acc)[4]) -> float {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wr[i >> 2][i & 3], relu(acc[i >> 2][i & 3]), s);
+    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(wr[i >> 2][i & 3], hterm(acc[i >> 2][i & 3]), s);
     return s;
   };
 
@@ -456,39 +567,62 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     uint16_t mb;
     float ks;    // FP8: the key's scale (lane l <-> key s0 + l)
     bool live;
+    int lo;      // |S| form: LDS offset (floats) of this wave's 64 linear terms in lin
   };
   struct Slice {  // values carried between the slices of one hand-off
     uint32_t x0, x1, y0, y1;
-    float v, mf;
+    float v, mf, ln;
   };
-  auto insert_slice = [&](const Unit& u, int i, Slice& z) {
+  // Hand-off modes: kFull (all slices); kEarly, the lane combine alone
+  // (slices 0-5 leave the unit's head-reduced sums in z.v and its mask
+  // values in z.mf); kLate, the rest (slices 0, 5, 6, 7: linear term, k
+  // scale, mask, range, insert).  The |S| form splits the unit of keys 0-63
+  // so: combined before the tile barrier, finished after it, which keeps
+  // two values per lane across the barrier instead of four partial sums.
+  constexpr int kFull = 0, kEarly = 1, kLate = 2;
+  auto insert_slice = [&](const Unit& u, int i, int mode, Slice& z) {
+    const bool comb = mode != kLate, fin = mode != kEarly;
     if (i == 0) {
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u.p[0]), __float_as_uint(u.p[2]), false, false);
-      z.x0 = r[0]; z.x1 = r[1];
-      asm volatile("" : "+v"(z.x0), "+v"(z.x1));
+      if (AB && fin) z.ln = lin[u.lo + lane];  // used in slice 5
+      if (comb) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u.p[0]), __float_as_uint(u.p[2]), false, false);
+        z.x0 = r[0]; z.x1 = r[1];
+        asm volatile("" : "+v"(z.x0), "+v"(z.x1));
+      }
     } else if (i == 1) {
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u.p[1]), __float_as_uint(u.p[3]), false, false);
-      z.y0 = r[0]; z.y1 = r[1];
-      asm volatile("" : "+v"(z.y0), "+v"(z.y1));
+      if (comb) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(u.p[1]), __float_as_uint(u.p[3]), false, false);
+        z.y0 = r[0]; z.y1 = r[1];
+        asm volatile("" : "+v"(z.y0), "+v"(z.y1));
+      }
     } else if (i == 2) {
-      z.x0 = __float_as_uint(__uint_as_float(z.x0) + __uint_as_float(z.x1));
-      asm volatile("" : "+v"(z.x0));
+      if (comb) {
+        z.x0 = __float_as_uint(__uint_as_float(z.x0) + __uint_as_float(z.x1));
+        asm volatile("" : "+v"(z.x0));
+      }
     } else if (i == 3) {
-      z.y0 = __float_as_uint(__uint_as_float(z.y0) + __uint_as_float(z.y1));
-      asm volatile("" : "+v"(z.y0));
+      if (comb) {
+        z.y0 = __float_as_uint(__uint_as_float(z.y0) + __uint_as_float(z.y1));
+        asm volatile("" : "+v"(z.y0));
+      }
     } else if (i == 4) {
-      auto r = __builtin_amdgcn_permlane16_swap(z.x0, z.y0, false, false);
-      z.x0 = r[0]; z.x1 = r[1];
-      asm volatile("" : "+v"(z.x0), "+v"(z.x1));
-      if (MK) {
-        z.mf = f16_bits_to_f32(u.mb);
-        asm volatile("" : "+v"(z.mf));
+      if (comb) {
+        auto r = __builtin_amdgcn_permlane16_swap(z.x0, z.y0, false, false);
+        z.x0 = r[0]; z.x1 = r[1];
+        asm volatile("" : "+v"(z.x0), "+v"(z.x1));
+        if (MK) {
+          z.mf = f16_bits_to_f32(u.mb);
+          asm volatile("" : "+v"(z.mf));
+        }
       }
     } else if (i == 5) {
-      z.v = __uint_as_float(z.x0) + __uint_as_float(z.x1);
-      if (F8) z.v = z.v * u.ks;
+      if (comb) z.v = __uint_as_float(z.x0) + __uint_as_float(z.x1);
+      if (fin) {
+        if (AB) z.v = z.v + z.ln;
+        if (F8) z.v = z.v * u.ks;
+      }
       asm volatile("" : "+v"(z.v));
-    } else if (i == 6) {
+    } else if (i == 6 && fin) {
       if (MK) z.v = z.v + z.mf;
       // lanes whose key lies outside [wlo, whi) (or all, for a dead unit)
       const int l0 = wlo - u.s0, l1 = whi - u.s0;
@@ -497,11 +631,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       const uint64_t inr = u.live ? (below_hi & ~below_lo) : 0ull;
       z.v = lane_select(inr, z.v, -__builtin_inff());
       asm volatile("" : "+v"(z.v));
-    } else if (i == 7 && SC) {
+    } else if (i == 7 && fin && SC) {
       // 64 consecutive keys per store: 256 contiguous bytes of the row
       const int s = u.s0 + lane;
       if (u.live && has_q && s < n_kv) __builtin_nontemporal_store(z.v, a.scores + t * a.scores_ld + s);
-    } else if (i == 7) {
+    } else if (i == 7 && fin) {
       const bool pass = z.v >= st.tau_v;
       const uint64_t m = ballot(pass);
       if (m != 0ull) {
@@ -519,7 +653,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   };
   // Make room for one more unit: compaction to the k_top best when fewer than
   // 128 free slots remain (rare once the stream is long).
-  auto room = [&]() {
+  auto room = [&]() __attribute__((always_inline)) {
     if (SC) return;
     st.count = __builtin_amdgcn_readfirstlane(st.count);  // keep it scalar (see uniform_u64)
     if (prefill_room(st.count, st.cap)) wave_topk_trim(st);
@@ -535,7 +669,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     if (SC) return;
     if (lane == 0) cflag[(it & 1) * NW + wv] = prefill_flag(st.count, st.cap) ? 1u : 0u;
   };
-  auto sync_compact = [&](int it) {
+  // `after` runs behind a compaction: it reads the next tile's first
+  // fragments and the linear term's A operand again, so that they need no
+  // registers while the compaction runs (it is the kernel's register peak).
+  auto sync_compact = [&](int it, auto&& after) {
     if (SC) return;
     uint32_t any = 0;
 #pragma unroll
@@ -543,6 +680,58 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     if (__builtin_amdgcn_readfirstlane(any)) {
       st.count = __builtin_amdgcn_readfirstlane(st.count);
       wave_topk_trim(st);
+      after();
+    }
+  };
+
+  // The linear term of one 16-key block for the workgroup's queries (|S|
+  // form), computed by every wave at the same steps of a tile for its own
+  // block(s) wv + NW k, so that no step branches on the wave index (a branch
+  // there makes the compiler drain every LDS read at its join).  The block's
+  // fragments are read from the tile in LDS (lin_load, early in a step) and
+  // fed to four MFMAs at the step's end (lin_mma): B as f16 (FP8: converted
+  // exactly, the k dimension mapped as in the FP8 MFMA, lane group G holding
+  // dims 32 G ... + 31, which the A rows follow).  Lanes of group G then
+  // store queries 2 G and 2 G + 1 (high + low part, times 2^-e) for key
+  // 16 blk + r16, one step later.
+  struct LinIn {
+    T b[KS];
+  };
+  auto lin_load = [&](int buf, int blk, LinIn& li) {
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(buf ? ktile1 : ktile0) + blk * kBlockBytes;
+#pragma unroll
+    for (int j = 0; j < KS; ++j) li.b[j] = frag(kt, j);
+  };
+  auto lin_mma = [&](const LinIn& li) -> f32x4 {
+    f16x8 bl[4];
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t wd = (uint32_t)li.b[0][2 * j + m];  // bytes 8 j + 4 m ... + 3
+          const auto lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.f, false);
+          const auto hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.f, true);
+          bl[j][4 * m] = lo2[0];
+          bl[j][4 * m + 1] = lo2[1];
+          bl[j][4 * m + 2] = hi2[0];
+          bl[j][4 * m + 3] = hi2[1];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bl[j] = __builtin_bit_cast(f16x8, li.b[j]);
+    }
+    f32x4 c = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(AL[j], bl[j], c, 0, 0, 0);
+    return c;
+  };
+  f32x4 lacc[2];  // linear terms of this wave's blocks, between their MFMAs and their store
+  auto lin_store = [&](const f32x4& c, int par, int blk) {
+    if (2 * G < NW) {
+      float* dst = lin + (par * NW + 2 * G) * TN + 16 * blk + r16;
+      dst[0] = (c[0] + c[1]) * lsc[0];
+      dst[TN] = (c[2] + c[3]) * lsc[1];
     }
   };
 
@@ -556,11 +745,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // of ops next to its MFMA; without them instruction selection moves the
   // whole epilogue behind the last MFMA).
   auto step = [&](const T (&bq)[KS], T (&nxt)[KS], bool load_next, int nbuf, int nblk, f32x4 (&acc)[4],
-                  const f32x4 (&prev)[4], const Unit* u, auto&& mid) -> float {
+                  const f32x4 (&prev)[4], const Unit* u, int umode, Slice& z, int lk, int ls, auto&& mid) -> float {
     const unsigned char* kn = reinterpret_cast<const unsigned char*>(nbuf ? ktile1 : ktile0) + nblk * kBlockBytes;
     const f32x4 zero = {};
     float sum = 0.f;
-    Slice z;
+    // linear term (|S| form): lk >= 0 reads block wv + NW lk of this tile
+    // here and issues its MFMAs at the end of the step (into lacc[lk]); ls >=
+    // 0 stores lacc[ls] at the end of the step
+    LinIn li;
+    if (AB && lk >= 0) lin_load(nbuf, wv + NW * lk, li);
     if constexpr (F8) {
       // four MFMAs (one per row block of 16 heads, the whole head dimension
       // each), four terms of the head reduction and two hand-off slices after
@@ -571,16 +764,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * rb + e;
-          sum = __builtin_fmaf(wr[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
+          sum = __builtin_fmaf(wr[i >> 2][i & 3], hterm(prev[i >> 2][i & 3]), sum);
           asm volatile("" : "+v"(sum));
         }
         if (load_next && rb == 0) nxt[0] = frag(kn, 0);
         if (u) {
-          insert_slice(*u, 2 * rb, z);
-          insert_slice(*u, 2 * rb + 1, z);
+          insert_slice(*u, 2 * rb, umode, z);
+          insert_slice(*u, 2 * rb + 1, umode, z);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (rb == 0) mid();
+        if (rb == 3 && AB && ls >= 0) lin_store(lacc[ls], nbuf, wv + NW * ls);
+        if (rb == 3 && AB && lk >= 0) lacc[lk] = lin_mma(li);
       }
     } else {
 #pragma unroll
@@ -589,12 +784,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
         for (int rb = 0; rb < 4; ++rb) {
           const int i = 4 * j + rb;
           acc[rb] = M::run(A[rb][j], bq[j], j == 0 ? zero : acc[rb]);
-          sum = __builtin_fmaf(wr[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
+          sum = __builtin_fmaf(wr[i >> 2][i & 3], hterm(prev[i >> 2][i & 3]), sum);
           asm volatile("" : "+v"(sum));
           if (load_next && j == 0) nxt[rb] = frag(kn, rb);
-          if (u) insert_slice(*u, i, z);
+          if (u) insert_slice(*u, i, umode, z);
           __builtin_amdgcn_sched_barrier(0);
           if (i == 3) mid();
+          if (i == 15 && AB && ls >= 0) lin_store(lacc[ls], nbuf, wv + NW * ls);
+          if (i == 15 && AB && lk >= 0) lacc[lk] = lin_mma(li);
         }
       }
     }
@@ -623,6 +820,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (AB) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) AL[j] = al_frag(j);
+    lsc[0] = 2 * G < NW ? __builtin_ldexpf(1.f, -les[2 * G]) : 0.f;
+    lsc[1] = 2 * G + 1 < NW ? __builtin_ldexpf(1.f, -les[2 * G + 1]) : 0.f;
+  }
   f32x4 accA[4], accB[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
@@ -632,13 +835,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   if (ntile > 0) frags(0, 0, bq0);
   const auto no_mid = [] {};
   Unit u0, u1;  // keys 0-63 and 64-127 of a tile
+  Slice z0, zt;  // the hand-off of u0 (kept from its early to its late part), any other
+  z0.v = 0.f;
+  z0.mf = 0.f;
   u1.p[0] = u1.p[1] = u1.p[2] = 0.f;
   u1.mb = 0;
   u1.ks = 1.f;
+  u1.lo = 0;
+  u0.p[0] = u0.p[1] = u0.p[2] = u0.p[3] = 0.f;
+  u0.s0 = 0;
+  u0.mb = 0;
+  u0.ks = 1.f;
+  u0.live = false;
+  u0.lo = 0;
   // Pipeline over the eight 16-key blocks of each tile: step b issues the
   // MFMAs of block b and finishes the head reduction of block b - 1.  The 64
   // scores of blocks 0-3 are handed to the top-k during the step of block 5,
-  // those of blocks 4-7 during the step of block 1 of the next tile.
+  // those of blocks 4-7 during the step of block 1 of the next tile.  In the
+  // |S| form both wait for the tile barrier, which makes every wave's linear
+  // terms of the tile visible: blocks 0-3 go during the step of block 1 of
+  // the next tile (their unit's fields are rewritten only after it), blocks
+  // 4-7 during the step of block 2.
   // The tile barrier sits inside the step of block 7, after its first four
   // MFMAs (block 7's fragments are in registers by then, so every wave is
   // done reading this tile's buffer): right after it each wave reads block
@@ -658,20 +875,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
       kset[buf ^ 1][0] = kload((tile + 1) * TN);
       kset[buf ^ 1][1] = kload((tile + 1) * TN + 64);
     }
-    u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr, no_mid);
+    u1.p[3] = step(bq0, bq1, true, buf, 1, accA, accB, nullptr, kFull, zt, -1, -1, no_mid);
     u1.s0 = (tile - 1) * TN + 64;
     u1.live = it > 0;
-    u0.p[0] = step(bq1, bq0, true, buf, 2, accB, accA, &u1, no_mid);
-    u0.p[1] = step(bq0, bq1, true, buf, 3, accA, accB, nullptr, no_mid);
-    u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr, no_mid);
-    u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr, no_mid);
+    u0.p[0] = step(bq1, bq0, true, buf, 2, accB, accA, AB ? &u0 : &u1, AB ? kLate : kFull, AB ? z0 : zt, -1, -1, no_mid);
+    u0.p[1] = step(bq0, bq1, true, buf, 3, accA, accB, AB ? &u1 : nullptr, kFull, zt, -1, -1, no_mid);
+    u0.p[2] = step(bq1, bq0, true, buf, 4, accB, accA, nullptr, kFull, zt, 0, -1, no_mid);
+    u0.p[3] = step(bq0, bq1, true, buf, 5, accA, accB, nullptr, kFull, zt, NW < 8 ? 1 : -1, 0, no_mid);
     u0.s0 = tile * TN;
     u0.mb = mset[buf][0];
     u0.ks = kset[buf][0];
     u0.live = true;
-    u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0, no_mid);
-    u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr, no_mid);
-    u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr, [&] {
+    u0.lo = (buf * NW + wv) * TN;
+    u1.p[0] = step(bq1, bq0, true, buf, 6, accB, accA, &u0, AB ? kEarly : kFull, z0, -1, -1, no_mid);
+    u1.p[1] = step(bq0, bq1, true, buf, 7, accA, accB, nullptr, kFull, zt, -1, NW < 8 ? 1 : -1, no_mid);
+    u1.p[2] = step(bq1, bq0, false, buf, 0, accB, accA, nullptr, kFull, zt, -1, -1, [&] {
       flag_need(it);
       // this wave's part of the next tile has landed in LDS: every vector
       // memory operation but the kAfterCopy issued after the copy is done
@@ -684,7 +902,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     });
     u1.mb = mset[buf][1];
     u1.ks = kset[buf][1];
-    sync_compact(it);
+    u1.lo = (buf * NW + wv) * TN + 64;
+    sync_compact(it, [&] {
+      if (more) frags(buf ^ 1, 0, bq0);
+      if constexpr (AB) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) AL[j] = al_frag(j);
+      }
+    });
   };
   for (int it = 0; it < ntile; it += 2) {
     tile_body(it, 0);
@@ -695,10 +920,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
     u1.p[3] = epilogue(accB);
     u1.s0 = (c1 - 1) * TN + 64;
     u1.live = true;
-    room();
-    Slice z;
+    if (AB) {
+      room();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) insert_slice(u1, i, z);
+      for (int i = 0; i < 8; ++i) insert_slice(u0, i, kLate, z0);
+    }
+    room();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) insert_slice(u1, i, kFull, zt);
   }
 
   if (SC) return;  // score-only mode: nothing to finish
@@ -819,7 +1048,8 @@ hipError_t launch_one(const KArgs& a, hipStream_t st) {
 
 // dynamic part only; the two key tiles (2 x 32 KiB) are static LDS
 size_t prefill_lds_bytes(int nw, int cap) {
-  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 4 + 16;
+  return (size_t)nw * cap * 8 + (size_t)nw * 256 * 4 + 2 * (size_t)nw * 4 + 16 + 2 * (size_t)nw * TN * 4 +
+         16 * D * 2 + 4 * (size_t)nw;
 }
 
 hipError_t launch_prefill(const KArgs& a, int nw, hipStream_t st) {

@@ -26,9 +26,11 @@ constexpr int kTrimSlack = 64;    // an in-stream trim keeps at most this many k
 // at most max(cap - 3 * 64 (not flagged), K + kTrimSlack (trimmed or too
 // short to trim)) keys, and two units must then fit, each with 128 free
 // slots in front of it: so cap >= K + kTrimSlack + 3 * 64.  Above that, 2 K
-// + 192 slots leave room for longer runs between trims at large K.
+// + 184 slots leave room for longer runs between trims at large K (184: with
+// K = 512, eight such buffers fit in LDS beside the key tiles and the linear
+// terms of the prefill kernel).
 constexpr int prefill_cap(int K) {
-  return 2 * K + 192 > K + kTrimSlack + (kUnitsPerTile + 1) * kUnitKeys ? 2 * K + 192
+  return 2 * K + 184 > K + kTrimSlack + (kUnitsPerTile + 1) * kUnitKeys ? 2 * K + 184
                                                                         : K + kTrimSlack + (kUnitsPerTile + 1) * kUnitKeys;
 }
 

@@ -51,9 +51,9 @@ MUTATIONS = {
                            "return count > cap - kUnitsPerTile * kUnitKeys;"),
     # the trim trigger one unit looser: a flagged buffer keeps too many keys
     "trim one unit late": ("return count > K + kTrimSlack;", "return count > K + kTrimSlack + kUnitKeys;"),
-    # capacity without the trim slack (2 K + 192 alone): small k_top overflow
+    # capacity without the trim slack (2 K + 184 alone): small k_top overflow
     "capacity without slack": ("constexpr int prefill_cap(int K) {\n  return",
-                               "constexpr int prefill_cap(int K) {\n  return 2 * K + 192;\n  return"),
+                               "constexpr int prefill_cap(int K) {\n  return 2 * K + 184;\n  return"),
 }
 
 

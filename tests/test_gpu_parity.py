@@ -320,7 +320,7 @@ def test_adversarial_ascending_scores(lid, k_top):
     (the streaming buffer is cut back again and again).  With a small k_top a
     trimmed buffer still holds up to k_top + 64 keys, and the next tile's two
     hand-offs touch 128 slots each past their count: the buffer capacity must
-    cover that (the 2 k_top + 192 slots alone did not below k_top 64)."""
+    cover that (the 2 k_top + 184 slots alone did not below k_top 64)."""
     n_tok, n_kv = 9, 20000
     q = np.zeros((n_tok, 64, 128), np.float16)
     q[:, :, 0] = 1.0
