@@ -345,8 +345,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
   // is the kernel's register peak and so runs without them).  Wavefront b % NW computes the term for block b of
   // every tile and hands it to the others through LDS: lin[tile parity]
   // [query][key of the tile].  bf16 keys keep the v_med3 form (their parts
-  // would need three bf16 rows).
-  constexpr bool AB = DT != 2;
+  // would need three bf16 rows), and so does the f16 kernel with 4
+  // wavefronts (k_top > 512), which has no registers for the term's A operand.
+  constexpr bool AB = DT == 3 || (DT == 1 && NW == 8);
   float* lin = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(cflag) + 2 * NW * 4 + 16);
   unsigned char* als = reinterpret_cast<unsigned char*>(lin + 2 * NW * TN);
   int* les = reinterpret_cast<int*>(als + 16 * D * 2);  // e of each query
