@@ -99,6 +99,26 @@ def test_exact_arithmetic_bit_exact(lid, plan, splits, dtype):
     parity(lid, q, k, w, None, ranges, 512, dtype, plan, splits, exact=True, label=f"exact/{dtype}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_weight_scales_per_query(lid, splits):
+    """The prefill kernel's |S| form carries each query's linear term
+    q~ = (1/2) sum_h w_h q_h in f16 high and low parts scaled by a power of two
+    of the query's own.  Queries of one workgroup with weights 2^-60 and 2^40
+    times the others' (exact inputs, so every score is still exact in f32)
+    must come out bit for bit: a scale shared by the workgroup would flush the
+    small query's parts to zero.  Each row is checked on its own, so the
+    tolerance follows that row's magnitude."""
+    n_tok, n_kv = 16, 3000
+    q, k, w = exact_inputs(n_tok, n_kv, seed=40 + splits, dtype="f16")
+    w = w.copy()
+    w[3] *= np.float32(2.0 ** -60)
+    w[5] *= np.float32(2.0 ** 40)
+    w[12] *= np.float32(2.0 ** -60)
+    w[13] = np.float32(0.0)  # no linear term at all
+    for r in (3, 5, 12, 13, 0):
+        parity(lid, q, k, w, None, None, 128, "f16", 2, splits, rows=[r], exact=True, label=f"w-scale/row{r}")
+
+
 @pytest.mark.parametrize("splits,k_top", [(3, 200), (4, 512), (5, 300), (6, 256), (20, 512), (3, 1000), (4, 100),
                                           (16, 512), (3, 301)])
 def test_prefill_split_finish_forms(lid, splits, k_top):
