@@ -81,6 +81,7 @@ static_assert(kSharedSelectKeys % BS == 0, "whole registers of keys per thread")
 
 template <int DT, bool MK, bool RG>
 __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchunk) {
+  constexpr bool AB = !RG;  // the |S| form of the head reduction (below)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   using M = MfmaS<DT>;
   using T = typename M::T;
@@ -190,6 +191,36 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
       }
     };
 
+    // |S| form: U = (1/2) (sum_t sum_h w |S| + Qt . k) with Qt = sum_t sum_h
+    // w_th q_th over the chunk (max(S, 0) = (S + |S|) / 2), so each head term
+    // is one FMA with |.| as a source modifier and the linear part is one dot
+    // product per key at the end.  Qt is accumulated from the staged q rows:
+    // wavefront wv takes dims 32 G + 8 (wv % 4) ... + 7 of heads 16 rb + r16
+    // for rb = 2 (wv / 4), 2 (wv / 4) + 1 (its LDS addresses depend on wv, so
+    // no step branches on it), summed over the chunk's queries in order.
+    // (The ranges form keeps max(S, 0): its range registers leave no room.)
+    const int qtj = wv & 3, qtr = 2 * (wv >> 2);
+    auto hterm = [](float x) -> float {
+      if constexpr (AB) return __builtin_fabsf(x);
+      else return relu(x);
+    };
+    float qacc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qacc[e] = 0.f;
+    T qa0, qa1;
+    float qw0 = 0.f, qw1 = 0.f;
+    auto qt_load = [&](int buf, int qi) {
+      qa0 = afrag(buf, qi, qtr, qtj);
+      qa1 = afrag(buf, qi, qtr + 1, qtj);
+      const float* wrow = reinterpret_cast<const float*>(smem + buf * kBufBytes + QB * kQBytes + qi * H * 4);
+      qw0 = wrow[16 * qtr + r16];
+      qw1 = wrow[16 * (qtr + 1) + r16];
+    };
+    auto qt_add = [&](int e) {
+      qacc[e] = __builtin_fmaf(qw0, (float)qa0[e], qacc[e]);
+      qacc[e] = __builtin_fmaf(qw1, (float)qa1[e], qacc[e]);
+    };
+
     T A[4][4];        // the current query's q fragments
     float wq[2][4][4];  // head weights of the even / odd queries of the chunk
     f32x4 accA[4], accB[4];
@@ -215,7 +246,7 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
         for (int rb = 0; rb < 4; ++rb) {
           const int i = 4 * j + rb;
           acc[rb] = M::run(A[rb][j], Bk[b][j], j == 0 ? zero : acc[rb]);
-          sum = __builtin_fmaf(wp[i >> 2][i & 3], relu(prev[i >> 2][i & 3]), sum);
+          sum = __builtin_fmaf(wp[i >> 2][i & 3], hterm(prev[i >> 2][i & 3]), sum);
           asm volatile("" : "+v"(sum));
           after(i);
           __builtin_amdgcn_sched_barrier(0);
@@ -280,7 +311,11 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
         float (&wc)[4][4] = wq[qi & 1];        // this query's weights
         float (&wo)[4][4] = wq[(qi & 1) ^ 1];  // the previous query's, then the next one's
         step(0, accA, accB, wo, P[3], nothing);
-        step(1, accB, accA, wc, P[0], nothing);
+        step(1, accB, accA, wc, P[0], [&](int i) {
+          if (!AB) return;
+          if (i == 0) qt_load(buf, qi);
+          else if (i >= 8) qt_add(i - 8);
+        });
         step(2, accA, accB, wc, P[1], nothing);
         // the last block: the next query's fragments are read behind its
         // MFMAs: the first k-step's four (and the weights) after the first
@@ -310,8 +345,45 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
       const float (&wl)[4][4] = wq[(nq - 1) & 1];
       float sum = P[3];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum = __builtin_fmaf(wl[i >> 2][i & 3], relu(accB[i >> 2][i & 3]), sum);
+      for (int i = 0; i < 16; ++i) sum = __builtin_fmaf(wl[i >> 2][i & 3], hterm(accB[i >> 2][i & 3]), sum);
       P[3] = sum;
+    }
+    if constexpr (AB) {
+    // The linear part: the 16 lanes of a group hold the same dims of
+    // different heads (xor butterfly adds them), the wavefronts' parts meet
+    // in LDS (the staging buffers are free once every wavefront is past its
+    // last query), and each lane adds Qt . k over its group's 32 dims to its
+    // keys' sums; the lane combine below adds the groups.
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = qacc[e];
+      x += __uint_as_float(xor_lane_u32<1>(__float_as_uint(x)));
+      x += __uint_as_float(xor_lane_u32<2>(__float_as_uint(x)));
+      x += __uint_as_float(xor_lane_u32<4>(__float_as_uint(x)));
+      x += __uint_as_float(xor_lane_u32<8>(__float_as_uint(x)));
+      qacc[e] = x;
+    }
+    float* part = reinterpret_cast<float*>(smem);  // [wavefront][dim]
+    if (r16 == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[wv * D + 32 * G + 8 * qtj + e] = qacc[e];
+    }
+    __syncthreads();
+    float qt[4][8];  // Qt at dims 32 G + 8 j + e: heads 0-31 from wavefront j, 32-63 from 4 + j
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qt[j][e] = part[j * D + 32 * G + 8 * j + e] + part[(4 + j) * D + 32 * G + 8 * j + e];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float d = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qt[j][e], (float)Bk[b][j][e], d);
+      P[b] += d;
+    }
     }
   }
   // Add the four head groups of each key: two permlane32 swaps add lane
@@ -325,7 +397,9 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
     const uint32_t x = __float_as_uint(__uint_as_float(r0[0]) + __uint_as_float(r0[1]));
     const uint32_t y = __float_as_uint(__uint_as_float(r1[0]) + __uint_as_float(r1[1]));
     const auto r2 = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-    usum = (__uint_as_float(r2[0]) + __uint_as_float(r2[1])) + msum;
+    usum = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+    if (AB) usum = 0.5f * usum;  // |S| form: twice the sum
+    usum = usum + msum;
     const int s = ks0 + lane;
     if (s < L || s >= R) usum = -__builtin_inff();
   }
