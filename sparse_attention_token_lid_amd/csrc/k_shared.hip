@@ -81,7 +81,7 @@ static_assert(kSharedSelectKeys % BS == 0, "whole registers of keys per thread")
 
 template <int DT, bool MK, bool RG>
 __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchunk) {
-  constexpr bool AB = !RG;  // the |S| form of the head reduction (below)
+  constexpr bool AB = true;  // the |S| form of the head reduction (below; kept switchable)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   using M = MfmaS<DT>;
   using T = typename M::T;
@@ -183,8 +183,11 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
     };
     auto rload = [&](int64_t t, int (&r)[2]) {
       if (RG) {
-        r[0] = a.kv_range[2 * t];
-        r[1] = a.kv_range[2 * t + 1];
+        // wave-uniform: scalar loads (into SGPRs, read-only data)
+        typedef const __attribute__((address_space(4))) int* cint_p;
+        const cint_p kr = (cint_p)(a.kv_range);
+        r[0] = kr[2 * t];
+        r[1] = kr[2 * t + 1];
       } else {
         r[0] = 0;
         r[1] = n_kv;
@@ -198,7 +201,6 @@ __global__ __launch_bounds__(BS, 1) void shared_scores_kernel(KArgs a, int qchun
     // wavefront wv takes dims 32 G + 8 (wv % 4) ... + 7 of heads 16 rb + r16
     // for rb = 2 (wv / 4), 2 (wv / 4) + 1 (its LDS addresses depend on wv, so
     // no step branches on it), summed over the chunk's queries in order.
-    // (The ranges form keeps max(S, 0): its range registers leave no room.)
     const int qtj = wv & 3, qtr = 2 * (wv >> 2);
     auto hterm = [](float x) -> float {
       if constexpr (AB) return __builtin_fabsf(x);
