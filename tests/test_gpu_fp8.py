@@ -123,6 +123,25 @@ def test_fp8_generic(lid, H, D, n_tok):
     parity_fp8(lid, q8, qs, k8, ks, w, None, None, 100, exact=True, label=f"generic/H{H}")
 
 
+def test_fp8_prefill_scales_per_query(lid):
+    """The FP8 prefill kernel's |S| form carries each query's linear term in
+    f16 parts scaled by a power of two of its own.  Queries of one workgroup
+    whose q scales are 2^-60 and 2^40 times the others' (and one with zero
+    weights), exact inputs: every row bit for bit, each checked on its own."""
+    rng = np.random.default_rng(77)
+    n_tok, n_kv = 16, 3000
+    q8, k8 = small_int_fp8(rng, (n_tok, 64, 128)), small_int_fp8(rng, (n_kv, 128))
+    qs = (2.0 ** rng.integers(-2, 3, (n_tok, 64))).astype(np.float32)
+    ks = (2.0 ** rng.integers(-2, 3, n_kv)).astype(np.float32)
+    w = rng.choice(np.array([0, 0.25, 0.5, 1, 2, -0.5], np.float32), (n_tok, 64))
+    qs[3] *= np.float32(2.0 ** -60)
+    qs[6] *= np.float32(2.0 ** 40)
+    w[9] = 0.0
+    for r in (3, 6, 9, 0):
+        parity_fp8(lid, q8, qs, k8, ks, w, None, None, 128, rows=[r], exact=True, label=f"prefill-scale/row{r}",
+                   plan=2, splits=1)
+
+
 @pytest.mark.parametrize("splits", [1, 3, 8, 20])
 def test_fp8_prefill_exact(lid, splits):
     """Prefill MFMA kernel with FP8 (v_mfma_f32_16x16x128_f8f6f4): small-integer
