@@ -325,10 +325,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_kernel(KArgs a) {
         if (has_q) v = *reinterpret_cast<const u32x4*>(qrow + (16 * rb + r16) * D + 32 * G + 8 * j);
         A[rb][j] = __builtin_bit_cast(T, v);
       }
+    // the weights of row t (row 0 without a query, whose A operand is zero
+    // and whose range is empty, so they never reach a score), loaded with no
+    // select behind them: a select right behind each load made the compiler
+    // wait for it, and for the q loads before it, one load at a time
+    const int64_t tw = has_q ? t : 0;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wr[rb][e] = has_q ? a.w[t * H + 16 * rb + 4 * G + e] : 0.f;
+      for (int e = 0; e < 4; ++e) wr[rb][e] = a.w[tw * H + 16 * rb + 4 * G + e];
   }
 
   // |S| form of the head reduction (f16 and FP8 keys).  max(S, 0) is
