@@ -20,7 +20,7 @@ namespace lid {
 
 constexpr int kUnitKeys = 64;     // keys handed to a wavefront's top-k at once
 constexpr int kUnitsPerTile = 2;  // hand-offs between two compaction points
-constexpr int kTrimSlack = 64;    // an in-stream trim keeps at most this many keys beyond K
+constexpr int kTrimSlack = 128;   // an in-stream trim keeps at most this many keys beyond K
 
 // Candidate slots per wavefront.  After a compaction point a buffer holds
 // at most max(cap - 3 * 64 (not flagged), K + kTrimSlack (trimmed or too

@@ -220,7 +220,7 @@ __device__ __forceinline__ DigitPick pick_digit(const uint32_t* hist, uint32_t n
 
 // ------------------------------------------------- per-wavefront streaming top-k
 // One wavefront owns one query's candidate buffer `buf` (LDS, capacity `cap`
-// >= K + 64).  Candidates with key > tau are appended; when the buffer would
+// >= K + 128).  Candidates with key > tau are appended; when the buffer would
 // overflow it is cut back to its K best (radix select of the K-th largest key,
 // which becomes the new tau).  Every key is unique, so "the K best" is exact.
 

@@ -334,13 +334,13 @@ def test_k_top_1024(lid):
         parity(lid, q, k, w, None, None, 1024, "f16", plan, 0, label="k1024")
 
 
-@pytest.mark.parametrize("k_top", [1, 7, 63, 512])
+@pytest.mark.parametrize("k_top", [1, 7, 63, 100, 512])
 def test_adversarial_ascending_scores(lid, k_top):
     """Scores that grow with the key index make every key a new top-k member
     (the streaming buffer is cut back again and again).  With a small k_top a
-    trimmed buffer still holds up to k_top + 64 keys, and the next tile's two
+    trimmed buffer still holds up to k_top + 128 keys, and the next tile's two
     hand-offs touch 128 slots each past their count: the buffer capacity must
-    cover that (the 2 k_top + 184 slots alone did not below k_top 64)."""
+    cover that (the 2 k_top + 184 slots alone do not below k_top 136)."""
     n_tok, n_kv = 9, 20000
     q = np.zeros((n_tok, 64, 128), np.float16)
     q[:, :, 0] = 1.0
