@@ -152,9 +152,9 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 // One workgroup of 4 wavefronts per (query t, tile of 64 heads); wavefront w
 // owns heads 16 w .. 16 w + 15 of the tile.  The selection is walked in
 // blocks of 32 entries.  Per block and wavefront, with v_mfma_f32_16x16x32:
-//   S^T (32 keys x 16 heads) = K_blk Q^T: A = key rows (16 B per lane) from
-//       a row-major LDS copy of the block, B = this wavefront's q rows, held
-//       in registers for the whole walk (16 k-steps of 32 dims);
+//   S^T (32 keys x 16 heads) = K_blk Q^T: A = key rows (16 B per lane, one
+//       ds_read_b128) from the block's rows in LDS, B = this wavefront's q
+//       rows, held in registers for the whole walk (16 k-steps of 32 dims);
 //   online softmax in f32: lane l has head l % 16 and the block's keys
 //       4 (l / 16) + i and 16 + 4 (l / 16) + i (i < 4), so a head's maximum
 //       and sum are two cross-lane steps; the running maximum is only moved
@@ -163,18 +163,23 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 //   O^T (512 dims x 16 heads) += K_blk^T P^T: the MFMA's k-slot
 //       8 (l / 16) + j is the key the lane already holds (4 (l / 16) + j, then
 //       16 + 4 (l / 16) + j - 4), so P^T never leaves the registers (the sum
-//       over k is order-free); A comes from a second, transposed LDS copy of
-//       the block whose rows (one per latent dim) list the keys in that
-//       order, so each A fragment is one 16-byte read.
-// Gathering: wavefront w loads the rows of keys 4 w .. 4 w + 3 and
-// 16 + 4 w .. 16 + 4 w + 3 (1 KiB per row per instruction), which are
-// exactly the 8 keys of one 16-byte chunk of the transposed rows, into
-// registers three blocks ahead (their indices four blocks ahead), and writes
-// both LDS copies (double-buffered) two blocks ahead.  The blocks are
-// software-pipelined: block b + 1's S^T and softmax run beside block b's
-// weighted sum.  The transposed rows (80 B pitch) swizzle their four chunks
-// by (dim / 8) mod 4 so that both the writes (lanes 8 dims apart) and the
-// reads (16 consecutive dims) spread over the banks.
+//       over k is order-free); A (16 dims x those 8 keys) is read from the same
+//       row-major rows by two transposing reads (ds_read_b64_tr_b16: in each
+//       16-lane group, lane i names 4 dims of key row i / 4 and receives one
+//       dim of all 4 rows), so the block is held in LDS once.
+// Gathering: the block's 32 rows go straight from global memory to LDS
+// (global_load_lds_dwordx4, one 1 KiB row per instruction, 8 per wavefront),
+// the row index broadcast from a vector load of the block's entries made one
+// block earlier; no register holds a row and no VALU touches one.  Two LDS
+// buffers: block b + 1 is gathered while block b is computed, and one barrier
+// per block (after the gather's completion wait) hands the buffers over.
+// Row j sits at 1 KiB x j and holds its 16-byte chunk c at position
+// c ^ (2 (j mod 8) + (j / 8 mod 2)) (the gather applies this by choosing which
+// chunk each lane fetches), which spreads both the 16-row column reads of S^T
+// and the 4-row transposing reads of O^T over the banks; every LDS address a
+// gather writes stays below 64 KiB.  64 KiB of LDS and at most 256 registers
+// per lane, so two workgroups share a compute unit and each hides the other's
+// barrier and dependency waits.
 // The weights are split into two 16-bit parts, p = hi + lo (lo = the
 // rounding residual of hi), and both are multiplied in, so the weighted sum
 // keeps about 16 bits of each weight instead of the 8 of a single bf16; the
@@ -183,15 +188,22 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 
 constexpr int kAL = 512;               // latent width of this path
 constexpr int kAKB = 32;               // selection entries per block
-constexpr int kAPitch = kAL + 8;       // row-major copy: row pitch in 16-bit elements (1040 B)
-constexpr int kATPitch = 40;           // transposed copy: row pitch in 16-bit elements (80 B)
+constexpr int kARowBytes = 2 * kAL;    // one gathered row
+constexpr int kABufBytes = kAKB * kARowBytes;   // one block's rows
 constexpr int kANks = kAL / 32;        // k-steps of S^T
 constexpr int kANdt = kAL / 16;        // 16-dim tiles of O^T
 constexpr float kAMaxSlack = 8.f;
 
+// chunk swizzle of block row j (0 <= j < 32): chunk c of the row is stored at
+// chunk position c ^ attn_swz(j); rows j and 16 + j share it
+__host__ __device__ constexpr int attn_swz(int j) { return 2 * (j & 7) + ((j >> 3) & 1); }
+static_assert(2 * kABufBytes <= 65536, "the gathers' LDS addresses must stay below 64 KiB");
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int DT> struct AMfma;
 template <> struct AMfma<1> {
@@ -218,20 +230,15 @@ template <> struct AMfma<2> {
   static __device__ __forceinline__ float from16(uint32_t b) { return __uint_as_float(b << 16); }
 };
 
-// block key of k-slot j (0..7) of lane group g (0..3)
-__device__ __forceinline__ int attn_key(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
-
 template <int DT>
-__global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t* __restrict__ qa,
+__global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(const uint16_t* __restrict__ qa,
                                                                   const uint16_t* __restrict__ kv,
                                                                   const int32_t* __restrict__ idx,
                                                                   float* __restrict__ out, int64_t n_kv, int H,
                                                                   int k_sel, float scale) {
   typedef AMfma<DT> M;
   typedef typename M::T T;
-  __shared__ __align__(16) uint16_t krow[2][kAKB][kAPitch];   // [buf][key][dim]
-  __shared__ __align__(16) uint16_t kt[2][kAL][kATPitch];     // [buf][dim][key, in k-slot order, swizzled]
-  __shared__ __align__(4) uint8_t vflag[2][kAKB];
+  __shared__ __align__(1024) unsigned char rows[2 * kABufBytes];   // [buf][row][chunk position]
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -255,72 +262,61 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
 
   const int32_t* irow = idx + t * (int64_t)k_sel;
   const int nb = (k_sel + kAKB - 1) / kAKB;
-  // a block's gathered rows in registers: keys attn_key(w, i), dims 8 lane ..
-  // 8 lane + 7, and their validity bits
-  struct Rows {
-    u32x4 st[8];
-    uint32_t vm;
+  // the selection entry 32 b + (lane mod 32) (clamped: k_sel >= 1 whenever a
+  // block exists), one vector load per block
+  auto load_idx = [&](int b) -> int32_t {
+    const int e = b * kAKB + (lane & (kAKB - 1));
+    return irow[e < k_sel ? e : k_sel - 1];
   };
-  // the selection entries of a block's rows, read one block ahead of the rows
-  // themselves by one vector load (lane i < 8 holds entry attn_key(w, i);
-  // clamped, so no branch: k_sel >= 1 whenever a block exists) and broadcast
-  // with readlane when the rows are fetched, so the row loads never wait on
-  // them (a scalar load would be waited for with the LDS reads)
-  int32_t ixv = 0;
-  auto load_idx = [&](int b) {
-    const int e = b * kAKB + attn_key(w, lane & 7);
-    ixv = irow[e < k_sel ? e : k_sel - 1];
+  // bit j: entry 32 b + j is in the selection and names a row
+  auto valid_mask = [&](int b, int32_t ix) -> uint32_t {
+    const int e = b * kAKB + (lane & (kAKB - 1));
+    return (uint32_t)__ballot(e < k_sel && ix >= 0 && (int64_t)ix < n_kv);
   };
-  auto fetch = [&](int b, Rows& R) {
-    uint32_t vm = 0;
+  // rows 8 w .. 8 w + 7 of a block into LDS buffer `buf` (invalid entries
+  // fetch row 0, which exists: a call with no keys walks no blocks)
+  const unsigned char* kvb = reinterpret_cast<const unsigned char*>(kv);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)rows;
+  // (lane l lands at chunk position l, so it fetches chunk l ^ attn_swz(j))
+  auto gather = [&](int buf, int32_t ix, uint32_t vm) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int e = b * kAKB + attn_key(w, i);
-      const int32_t ri = __builtin_amdgcn_readlane(ixv, i);
-      const bool v = e < k_sel && ri >= 0 && (int64_t)ri < n_kv;
-      vm |= (uint32_t)v << i;
-      const int64_t row = v ? ri : 0;
-      R.st[i] = *reinterpret_cast<const u32x4*>(kv + row * kAL + 8 * lane);
+      const int j = 8 * w + i;
+      const int32_t ri = __builtin_amdgcn_readlane(ix, j);
+      const int64_t row = ((vm >> j) & 1u) ? ri : 0;
+      dma_row4(kvb + row * kARowBytes, (uint32_t)(16 * (lane ^ attn_swz(j))),
+               lds0 + (uint32_t)(buf * kABufBytes + j * kARowBytes));
     }
-    R.vm = vm;
   };
-  auto stage = [&](int buf, const Rows& R) {
-    const u32x4* st = R.st;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(&krow[buf][attn_key(w, i)][8 * lane]) = st[i];
-    // transposed: dim 8 lane + c gets the 8 keys of chunk w (swizzled by lane & 3)
-    const int chunk = w ^ (lane & 3);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int q = c >> 1;
-      uint32_t x[4];
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const uint32_t a = st[2 * k2][q], b = st[2 * k2 + 1][q];
-        x[k2] = (c & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
-      }
-      *reinterpret_cast<u32x4*>(&kt[buf][8 * lane + c][8 * chunk]) = u32x4{x[0], x[1], x[2], x[3]};
-    }
-    if (lane < 8) vflag[buf][attn_key(w, lane)] = (uint8_t)((R.vm >> lane) & 1u);
-  };
+
+  // S^T reads row r (and 16 + r), chunk 4 ks + g; the transposing reads name
+  // row 4 g + r / 4 (and 16 + that), dims 16 d + 4 (r % 4) .. + 3, i.e. chunk
+  // 2 d + (r % 4) / 2, bytes 8 (r % 2) ..
+  const int s_row = r * kARowBytes, s_swz = attn_swz(r);
+  const int t_rowi = 4 * g + (r >> 2);
+  const int t_row = t_rowi * kARowBytes + 8 * (r & 1), t_swz = attn_swz(t_rowi), t_c = (r & 3) >> 1;
 
   f32x4 acc[kANdt];
 #pragma unroll
   for (int d = 0; d < kANdt; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_inff(), den = 0.f;
 
-  // S^T of a staged block: lane gets head r and keys 4 g + i (s0), 16 + 4 g + i
+  // S^T of a block: lane gets head r and keys 4 g + i (s0), 16 + 4 g + i
   // (s1); even and odd k-steps in separate chains
   auto scores = [&](int buf, f32x4& s0, f32x4& s1) {
+    const unsigned char* base = rows + buf * kABufBytes + s_row;
+    // (4 ks + g) ^ swz = 16 (ks / 4) + ((4 (ks % 4) + g) ^ swz): four per-lane
+    // bases, the rest an immediate offset
+    auto at = [&](int ks) { return base + 16 * ((4 * (ks & 3) + g) ^ s_swz) + 256 * (ks >> 2); };
     f32x4 s2 = {0.f, 0.f, 0.f, 0.f}, s3 = s2;
     s0 = s2;
     s1 = s2;
 #pragma unroll
     for (int ks = 0; ks < kANks; ks += 2) {
-      const T a0 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][r][32 * ks + 8 * g]));
-      const T a1 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][16 + r][32 * ks + 8 * g]));
-      const T a2 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][r][32 * ks + 32 + 8 * g]));
-      const T a3 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&krow[buf][16 + r][32 * ks + 32 + 8 * g]));
+      const T a0 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(at(ks)));
+      const T a1 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(at(ks) + 16 * kARowBytes));
+      const T a2 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(at(ks + 1)));
+      const T a3 = __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(at(ks + 1) + 16 * kARowBytes));
       s0 = M::run(a0, qf[ks], s0);
       s1 = M::run(a1, qf[ks], s1);
       s2 = M::run(a2, qf[ks + 1], s2);
@@ -332,14 +328,13 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
   // online softmax of a block's scores: moves the running maximum (rescaling
   // the accumulator and the denominator when it moves), adds the block's
   // weights to the denominator and returns them as the two 16-bit parts
-  auto softmax = [&](int buf, const f32x4& s0, const f32x4& s1, T& phi, T& plo) {
-    const uint32_t f0 = *reinterpret_cast<const uint32_t*>(&vflag[buf][4 * g]);
-    const uint32_t f1 = *reinterpret_cast<const uint32_t*>(&vflag[buf][16 + 4 * g]);
+  auto softmax = [&](uint32_t vm, const f32x4& s0, const f32x4& s1, T& phi, T& plo) {
+    const uint32_t f0 = vm >> (4 * g), f1 = vm >> (16 + 4 * g);
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = ((f0 >> (8 * i)) & 1u) ? scale * s0[i] : -__builtin_inff();
-      sv[4 + i] = ((f1 >> (8 * i)) & 1u) ? scale * s1[i] : -__builtin_inff();
+      sv[i] = ((f0 >> i) & 1u) ? scale * s0[i] : -__builtin_inff();
+      sv[4 + i] = ((f1 >> i) & 1u) ? scale * s1[i] : -__builtin_inff();
     }
     float bm = sv[0];
 #pragma unroll
@@ -373,14 +368,19 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     plo = __builtin_bit_cast(T, u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
                                       lo[6] | (lo[7] << 16)});
   };
-  // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot 8 g + j], one 16-byte read;
-  // the lo product of tile d - 1 is issued between the hi products of tiles d
-  // and d + 1, so no MFMA waits on the one just before it
+  // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot 8 g + j] from two
+  // transposing reads (keys 4 g .. 4 g + 3, then 16 + 4 g .. 16 + 4 g + 3);
+  // the lo product of tile d - 1 is issued between the hi products of tiles
+  // d and d + 1, so no MFMA waits on the one just before it
   auto weighted_sum = [&](int buf, const T& phi, const T& plo) {
+    const unsigned char* base = rows + buf * kABufBytes + t_row;
     auto afrag = [&](int d) {
-      const int dim = 16 * d + r;
-      const int chunk = g ^ ((dim >> 3) & 3);
-      return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(&kt[buf][dim][8 * chunk]));
+      // (2 d + c) ^ swz = 16 (d / 8) + ((2 (d % 8) + c) ^ swz): eight per-lane bases
+      const unsigned char* p = base + 16 * ((2 * (d & 7) + t_c) ^ t_swz) + 256 * (d >> 3);
+      const i16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 16 * kARowBytes));
+      const uint2 y0 = __builtin_bit_cast(uint2, x0), y1 = __builtin_bit_cast(uint2, x1);
+      return __builtin_bit_cast(T, u32x4{y0.x, y0.y, y1.x, y1.y});
     };
     T aprev = afrag(0);
     acc[0] = M::run(aprev, phi, acc[0]);
@@ -394,53 +394,41 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
     acc[kANdt - 1] = M::run(aprev, plo, acc[kANdt - 1]);
   };
 
-  // Software pipeline over the blocks: iteration b runs block b + 1's scores
-  // and softmax beside block b's weighted sum, so the softmax arithmetic and
-  // the LDS latencies overlap the MFMAs.  Both LDS buffers hold staged blocks
-  // (b and b + 1); block b + 2 is staged into b's buffers once every
-  // wavefront is done with them.  Rows are gathered three blocks ahead into
-  // two register sets used in turn (block j's rows in set j mod 2; the loop
-  // is unrolled by two so that the sets are fixed registers), their indices
-  // one block ahead of the rows.
-  Rows ra, rb;
-  T phi = {}, plo = {};
+  // Block b: gather block b + 1 into the other buffer (its entries were
+  // loaded one block earlier) and load block b + 2's entries, then compute
+  // block b; the completion wait and the barrier at the end make block b + 1
+  // visible and free block b's buffer for block b + 2.
+  int32_t ixn = 0;     // entries of the next block to gather
+  uint32_t vmc = 0;    // validity bits of the block being computed
   if (nb > 0) {
-    load_idx(0);
-    fetch(0, ra);
-    stage(0, ra);
-    if (nb > 1) {
-      load_idx(1);
-      fetch(1, rb);
-      stage(1, rb);
-    }
-    if (nb > 2) {
-      load_idx(2);
-      fetch(2, ra);
-    }
-    if (nb > 3) load_idx(3);
+    const int32_t ix0 = load_idx(0);
+    vmc = valid_mask(0, ix0);
+    gather(0, ix0, vmc);
+    if (nb > 1) ixn = load_idx(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    f32x4 s0, s1;
-    scores(0, s0, s1);
-    softmax(0, s0, s1, phi, plo);
   }
-  // rstage holds block b + 2's rows; rfetch (block b + 1's, staged) takes block b + 3's
-  auto block = [&](int b, const Rows& rstage, Rows& rfetch) {
-    const int buf = b & 1;
-    if (b + 3 < nb) fetch(b + 3, rfetch);
-    if (b + 4 < nb) load_idx(b + 4);
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-    if (b + 1 < nb) scores(buf ^ 1, s0, s1);
+  auto block = [&](int b, int buf) {
+    uint32_t vmn = 0;
+    if (b + 1 < nb) {
+      vmn = valid_mask(b + 1, ixn);
+      gather(buf ^ 1, ixn, vmn);
+      if (b + 2 < nb) ixn = load_idx(b + 2);
+    }
+    f32x4 s0, s1;
+    scores(buf, s0, s1);
+    T phi, plo;
+    softmax(vmc, s0, s1, phi, plo);
     weighted_sum(buf, phi, plo);
-    if (b + 1 < nb) softmax(buf ^ 1, s0, s1, phi, plo);
-    if (b + 2 < nb) {
-      __syncthreads();   // every wavefront is done with block b's buffers
-      stage(buf, rstage);
-      __syncthreads();   // block b + 2 is visible
+    vmc = vmn;
+    if (b + 1 < nb) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
   };
   for (int b = 0; b < nb; b += 2) {
-    block(b, ra, rb);
-    if (b + 1 < nb) block(b + 1, rb, ra);
+    block(b, 0);
+    if (b + 1 < nb) block(b + 1, 1);
   }
   // lane: head r, dims 16 d + 4 g .. + 3
   if (hok) {
@@ -451,7 +439,6 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_mfma_kernel(const uint16_t
       *reinterpret_cast<f32x4*>(o + 16 * d) = acc[d] * inv;
   }
 }
-
 }  // namespace
 
 hipError_t launch_sparse_attn(const void* qa, const void* kv, const int32_t* idx, float* out, int64_t n_tok,
