@@ -180,10 +180,13 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 // gather writes stays below 64 KiB.  64 KiB of LDS and at most 256 registers
 // per lane, so two workgroups share a compute unit and each hides the other's
 // barrier and dependency waits.
-// The weights are split into two 16-bit parts, p = hi + lo (lo = the
-// rounding residual of hi), and both are multiplied in, so the weighted sum
-// keeps about 16 bits of each weight instead of the 8 of a single bf16; the
-// denominator sums hi + lo, the weights actually applied.
+// The weights enter the O^T product rounded once to the operand type (bf16
+// or f16, as flash-attention kernels do), and the denominator sums the
+// rounded weights, so the output is an exact convex combination of the rows
+// with each weight off by its one rounding.  (Keeping a second 16-bit part,
+// p = hi + lo, would keep about 16 bits per weight at the price of a third
+// more MFMAs.)  The S^T phase runs at a raised wave priority: its LDS reads
+// are the latency the co-resident workgroup's MFMAs hide.
 // Invalid entries are gathered as row 0 and given s = -inf.
 
 constexpr int kAL = 512;               // latent width of this path
@@ -326,9 +329,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(const uint16_t
     s1 += s3;
   };
   // online softmax of a block's scores: moves the running maximum (rescaling
-  // the accumulator and the denominator when it moves), adds the block's
-  // weights to the denominator and returns them as the two 16-bit parts
-  auto softmax = [&](uint32_t vm, const f32x4& s0, const f32x4& s1, T& phi, T& plo) {
+  // the accumulator and the denominator when it moves), rounds the block's
+  // weights to the operand type, adds the rounded weights to the denominator
+  // and returns them
+  auto softmax = [&](uint32_t vm, const f32x4& s0, const f32x4& s1, T& phi) {
     const uint32_t f0 = vm >> (4 * g), f1 = vm >> (16 + 4 * g);
     float sv[8];
 #pragma unroll
@@ -344,15 +348,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(const uint16_t
     const float mn = bm > m + kAMaxSlack ? bm : m;   // m = -inf: takes bm
     const float mref = mn == -__builtin_inff() ? 0.f : mn;
     const float cf = __expf(m - mref);              // m = -inf: 0 (nothing accumulated yet)
-    uint32_t hi[8], lo[8];
+    uint32_t hi[8];
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = __expf(sv[j] - mref);         // invalid: exp(-inf) = 0
-      hi[j] = M::to16(p);
-      const float ph = M::from16(hi[j]);
-      lo[j] = M::to16(p - ph);
-      ps += ph + M::from16(lo[j]);
+      hi[j] = M::to16(__expf(sv[j] - mref));       // invalid: exp(-inf) = 0
+      ps += M::from16(hi[j]);
     }
     ps += __uint_as_float(xor_lane_u32<16>(__float_as_uint(ps)));
     ps += __uint_as_float(xor_lane_u32<32>(__float_as_uint(ps)));
@@ -365,14 +366,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(const uint16_t
     m = mn;
     phi = __builtin_bit_cast(T, u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
                                       hi[6] | (hi[7] << 16)});
-    plo = __builtin_bit_cast(T, u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
-                                      lo[6] | (lo[7] << 16)});
   };
   // O^T += K_blk^T P^T: A[m = dim 16 d + r][k-slot 8 g + j] from two
-  // transposing reads (keys 4 g .. 4 g + 3, then 16 + 4 g .. 16 + 4 g + 3);
-  // the lo product of tile d - 1 is issued between the hi products of tiles
-  // d and d + 1, so no MFMA waits on the one just before it
-  auto weighted_sum = [&](int buf, const T& phi, const T& plo) {
+  // transposing reads (keys 4 g .. 4 g + 3, then 16 + 4 g .. 16 + 4 g + 3)
+  auto weighted_sum = [&](int buf, const T& phi) {
     const unsigned char* base = rows + buf * kABufBytes + t_row;
     auto afrag = [&](int d) {
       // (2 d + c) ^ swz = 16 (d / 8) + ((2 (d % 8) + c) ^ swz): eight per-lane bases
@@ -382,16 +379,8 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(const uint16_t
       const uint2 y0 = __builtin_bit_cast(uint2, x0), y1 = __builtin_bit_cast(uint2, x1);
       return __builtin_bit_cast(T, u32x4{y0.x, y0.y, y1.x, y1.y});
     };
-    T aprev = afrag(0);
-    acc[0] = M::run(aprev, phi, acc[0]);
 #pragma unroll
-    for (int d = 1; d < kANdt; ++d) {
-      const T a = afrag(d);
-      acc[d] = M::run(a, phi, acc[d]);
-      acc[d - 1] = M::run(aprev, plo, acc[d - 1]);
-      aprev = a;
-    }
-    acc[kANdt - 1] = M::run(aprev, plo, acc[kANdt - 1]);
+    for (int d = 0; d < kANdt; ++d) acc[d] = M::run(afrag(d), phi, acc[d]);
   };
 
   // Block b: gather block b + 1 into the other buffer (its entries were
@@ -416,10 +405,12 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_mfma_kernel(const uint16_t
       if (b + 2 < nb) ixn = load_idx(b + 2);
     }
     f32x4 s0, s1;
+    __builtin_amdgcn_s_setprio(2);
     scores(buf, s0, s1);
-    T phi, plo;
-    softmax(vmc, s0, s1, phi, plo);
-    weighted_sum(buf, phi, plo);
+    __builtin_amdgcn_s_setprio(0);
+    T phi;
+    softmax(vmc, s0, s1, phi);
+    weighted_sum(buf, phi);
     vmc = vmn;
     if (b + 1 < nb) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
