@@ -175,9 +175,11 @@ __global__ __launch_bounds__(BS) void sparse_attn_kernel(const uint16_t* __restr
 // per block (after the gather's completion wait) hands the buffers over.
 // Row j sits at 1 KiB x j and holds its 16-byte chunk c at position
 // c ^ (2 (j mod 8) + (j / 8 mod 2)) (the gather applies this by choosing which
-// chunk each lane fetches), which spreads both the 16-row column reads of S^T
-// and the 4-row transposing reads of O^T over the banks; every LDS address a
-// gather writes stays below 64 KiB.  64 KiB of LDS and at most 256 registers
+// chunk each lane fetches), which leaves the 4-row transposing reads of O^T
+// free of bank conflicts; the 16-byte S^T reads of 16 rows at one column
+// still conflict two-way (a 16-byte read goes in 8-byte passes of 32 lanes,
+// and 1 KiB rows give those 32 reads only 16 chunk positions).  Every LDS
+// address a gather writes stays below 64 KiB.  64 KiB of LDS and at most 256 registers
 // per lane, so two workgroups share a compute unit and each hides the other's
 // barrier and dependency waits.
 // The weights enter the O^T product rounded once to the operand type (bf16
