@@ -220,6 +220,63 @@ def test_attn_after_topk(lid):
     check(lid, qa, kv, idx, 1.0 / np.sqrt(L), "bf16", "after topk")
 
 
+def _round16(x, dtype):
+    """f32 values rounded to nearest-even bf16 / f16, returned as f64."""
+    x = np.asarray(x, np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    b = x.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _to16(x, dtype):
+    """f32 values as the 16-bit array the binding takes (bf16: bit patterns)."""
+    x = np.asarray(x, np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    b = x.view(np.uint32).astype(np.uint64)
+    return (((b + 0x7FFF + ((b >> 16) & 1)) >> 16) & 0xFFFF).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attn_weight_rounding_exact(lid, dtype):
+    """Pins the latent-512 path's weight arithmetic, not only its bound: two
+    selected rows with scores 0 and c_h = -(h+1)/8 (q = c_h e_0; row A has 0
+    and row B 1 in dim 0) give weights 1 and p = exp(c_h), and the output must
+    be (kv_A + p~ kv_B) / (1 + p~) with p~ = p rounded once to the 16-bit
+    operand type, to f32 accuracy.  Weights kept in f32, or rounded another
+    way, are off by about 2^-9 (bf16) / 2^-12 (f16) of |kv_B - kv_A|.  Heads
+    whose f32 weight lies within 2^-20 of a rounding midpoint are skipped
+    (the GPU's exp may differ from numpy's by an ulp or two)."""
+    H, L, n_kv = 64, 512, 4
+    rng = np.random.default_rng(31)
+    kvf = rng.standard_normal((n_kv, L)).astype(np.float32)
+    kvf[1, 0], kvf[2, 0] = 0.0, 1.0
+    kv = _to16(kvf, dtype)
+    c = -(np.arange(H) + 1) / 8.0
+    qf = np.zeros((1, H, L), np.float32)
+    qf[0, :, 0] = c
+    qa = _to16(qf, dtype)
+    idx = np.array([[1, 2]], np.int32)
+    got = run(lid, qa, kv, idx, 1.0, dtype)[0].astype(np.float64)
+    kva, kvb = _f64(kv[1:2], dtype)[0], _f64(kv[2:3], dtype)[0]
+    p32 = np.exp(c.astype(np.float32)).astype(np.float32)
+    pt = _round16(p32, dtype)
+    near = _round16(p32 * np.float32(1 - 2.0 ** -20), dtype) != _round16(p32 * np.float32(1 + 2.0 ** -20), dtype)
+    want = (kva[None, :] + pt[:, None] * kvb[None, :]) / (1 + pt[:, None])
+    tol = 1e-6 * max(np.abs(kva).max(), np.abs(kvb).max())
+    heads = np.flatnonzero(~near)
+    assert heads.size >= 48, heads.size
+    err = np.abs(got[heads] - want[heads]).max()
+    _say(f"  weight rounding ({dtype}): {heads.size} heads, max err {err:.3e} (bound {tol:.3e})")
+    assert err <= tol
+    # the f32-weight result is far outside that bound: the check sees the rounding
+    p64 = p32.astype(np.float64)
+    f32w = (kva[None, :] + p64[:, None] * kvb[None, :]) / (1 + p64[:, None])
+    assert np.abs(f32w[heads] - want[heads]).max() > 100 * tol
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_attn_full_size_sampled(lid, dtype):
     """The bench shape (512 queries x 16384 keys, 64 heads, L 512, 512
